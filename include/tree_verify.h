@@ -1,0 +1,183 @@
+/*
+ * tree_verify.h -- C ABI of libtreeverify.so: tree-verification attention on MI355X (gfx950).
+ *
+ * One speculative-decoding step verifies a whole draft tree in a single target pass.  The
+ * tree is flattened into N nodes (node 0 = root = the last accepted token) described by a
+ * parent array.  Node i attends to every one of the L cached prefix positions and to tree
+ * position L + j exactly when j is i or an ancestor of i, and carries position id
+ * L + depth(i).  ("Tree attention mask for draft-tree verification", sections "TL;DR" and
+ * "A strong answer"; "Tree Verification", section "Tree Attention".)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers are plain host or device addresses as stated per argument; no entry point
+ *    allocates, frees or synchronises.  Device work is enqueued on the caller's stream and
+ *    is safe to capture in a HIP graph (sizes come from arguments, never from constants).
+ *  - Errors are returned as tv_status; a human-readable detail of the last error on the
+ *    calling thread is available from tv_last_error().  Nothing is written to outputs when
+ *    an argument check fails.
+ *  - N (nodes per tree, root included) is 1..TV_MAX_NODES.  The ancestor bitmask of node i
+ *    is one uint64 word with bit j set (LSB first) iff j is i or an ancestor of i.
+ *  - Device-resident parent arrays must satisfy parent[0] == -1 and 0 <= parent[i] < i
+ *    (any parent-before-child order is accepted; "Tree Verification", "Tree Attention").
+ *    The kernels never read out of bounds or loop forever on a violation; tree_meta_from_parent
+ *    flags the offending nodes (depth = pos = -1, bitmask = 0).
+ */
+#ifndef TREE_VERIFY_H
+#define TREE_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TV_MAX_NODES 64
+#define TV_ABI_VERSION 1
+
+typedef enum {
+  TV_OK = 0,
+  TV_ERR_INVALID_ARG = 1,     /* null pointer, bad size, stride or dtype             */
+  TV_ERR_INVALID_PATH = 2,    /* empty path or negative rank                          */
+  TV_ERR_MISSING_PARENT = 3,  /* a path whose one-shorter prefix is not a node         */
+  TV_ERR_CAPACITY = 4,        /* more nodes than the caller's arrays (or 64) can hold  */
+  TV_ERR_UNSUPPORTED = 5,     /* a shape the kernels do not implement (e.g. D = 96)    */
+  TV_ERR_WORKSPACE = 6,       /* workspace missing or smaller than required            */
+  TV_ERR_HIP = 7              /* a HIP runtime call failed (launch, attribute query)   */
+} tv_status;
+
+typedef enum { TV_BF16 = 0, TV_F32 = 1 } tv_dtype;
+typedef enum { TV_KV_CONTIGUOUS = 0, TV_KV_PAGED = 1 } tv_kv_layout;
+typedef enum { TV_PATH_AUTO = 0, TV_PATH_VALU = 1, TV_PATH_MFMA = 2 } tv_path;
+
+/*
+ * tree_meta_build -- host metadata builder ("Tree attention mask for draft-tree
+ * verification", section "A strong answer": rank-path candidates, node order, parent,
+ * depth, the ancestor mask and position ids prefix + depth).
+ *
+ * Input (host memory, read only):
+ *   ranks[path_off[p] .. path_off[p+1])  the drafter-rank tuple of candidate p, p < num_paths;
+ *                                        path_off has num_paths + 1 entries, path_off[0] = 0.
+ *   prefix_len                           L, the cached prefix length (>= 0).
+ *   max_nodes                            capacity of the output arrays (>= 1).
+ * Output (host memory, caller-owned, at least max_nodes entries each):
+ *   parent[i], depth[i], pos[i] = prefix_len + depth[i], bitmask[i] (one uint64 per node);
+ *   *num_nodes = N (root included).
+ *   *bad_path  = input index of the offending path on TV_ERR_INVALID_PATH /
+ *                TV_ERR_MISSING_PARENT, else -1.  (May be NULL.)
+ * Node order: distinct paths sorted by (length, lexicographic ranks); duplicates collapse.
+ * Errors: TV_ERR_INVALID_ARG (null pointers, num_paths < 0, bad offsets),
+ *         TV_ERR_INVALID_PATH, TV_ERR_MISSING_PARENT (the first in sorted order),
+ *         TV_ERR_CAPACITY (N > max_nodes or N > TV_MAX_NODES).  num_paths == 0 gives the
+ *         root alone (N = 1): plain decoding.  Outputs are unspecified on error.
+ */
+tv_status tree_meta_build(const int32_t* ranks, const int64_t* path_off, int32_t num_paths,
+                          int32_t prefix_len, int32_t max_nodes,
+                          int32_t* parent, int32_t* depth, uint64_t* bitmask, int32_t* pos,
+                          int32_t* num_nodes, int32_t* bad_path);
+
+/*
+ * tree_meta_from_parent -- the same metadata from device-resident parent arrays (the
+ * parent-array form a kernel "expands per tile": "Tree attention mask for draft-tree
+ * verification", paragraph after the build listing).
+ *
+ * Device memory: parent[b * parent_sb + i] (int32; parent_sb = 0 shares one tree across
+ * the batch), prefix_len[b] (int32; may be NULL, then pos = depth).
+ * Device outputs, dense [B, N]: depth (int32), bitmask (uint64), pos (int32); any of the
+ * three may be NULL to skip it.  Invalid nodes (see header comment) get -1 / 0 / -1.
+ * Errors: TV_ERR_INVALID_ARG (B < 0, N outside 1..64, parent NULL, parent_sb < 0),
+ *         TV_ERR_HIP.  B == 0 is a no-op.
+ */
+tv_status tree_meta_from_parent(const int32_t* parent, int32_t parent_sb, int32_t B,
+                                int32_t N, const int32_t* prefix_len, int32_t* depth,
+                                uint64_t* bitmask, int32_t* pos, hipStream_t stream);
+
+/*
+ * Arguments of tree_verify_attn.  All tensor pointers are device memory; strides are in
+ * elements; the last (D) dimension of q, k, v and out is contiguous.
+ *
+ *   q    [B, N, Hq, D]  at q + b*q_sb + i*q_sn + h*q_sh.
+ *   k, v logical token t of request b, kv head g:
+ *          contiguous: base + b*kv_sb + t*kv_st + g*kv_sh, t < prefix_len[b] + N;
+ *          paged:      base + page*kv_sb + (t % page_size)*kv_st + g*kv_sh with
+ *                      page = page_table[b*pages_per_seq + t / page_size].
+ *        Tree node j's key/value is logical token prefix_len[b] + j, in node order
+ *        ("Tree attention mask for draft-tree verification", section "What it costs").
+ *        Tokens at or beyond prefix_len[b] + N are never read.
+ *   parent [B, N] int32 at parent + b*parent_sb (parent_sb = 0: one shared tree).
+ *   prefix_len [B] int32, each in 0..max_prefix_len; max_prefix_len is a host-side upper
+ *        bound used only to size the grid (no device sync).
+ *   out  [B, N, Hq, D] (same dtype as q) at out + b*o_sb + i*o_sn + h*o_sh.
+ *   lse  [B, N, Hq] fp32, contiguous, natural log of the sum of exp(scores); may be NULL.
+ *   Query head h reads kv head h / (Hq / Hkv).  sm_scale = 0 means 1/sqrt(D).
+ *   workspace: device scratch of tree_verify_attn_workspace_size() bytes (may be 0 bytes,
+ *        then workspace may be NULL).  Contents need no initialisation.
+ *   num_splits: 0 = automatic, else the number of key-range splits per (request, kv head).
+ *   path: TV_PATH_AUTO picks the MFMA kernel for bf16 once N * (Hq / Hkv) >= 16, else the
+ *        VALU kernel; the others force one (MFMA needs bf16).
+ */
+typedef struct tv_attn_args {
+  int32_t dtype;           /* tv_dtype of q, k, v and out                                  */
+  int32_t B, N, Hq, Hkv, D;/* D in {64, 128}; 1 <= N <= 64; Hq % Hkv == 0                   */
+  const void* q;
+  int64_t q_sb, q_sn, q_sh;
+  int32_t kv_layout;       /* tv_kv_layout                                                  */
+  int32_t page_size;       /* paged only: tokens per page (>= 1)                           */
+  const void* k;
+  const void* v;
+  int64_t kv_sb, kv_st, kv_sh;
+  const int32_t* page_table;
+  int32_t pages_per_seq;   /* paged only: row length of page_table                          */
+  int32_t parent_sb;
+  const int32_t* parent;
+  const int32_t* prefix_len;
+  int32_t max_prefix_len;
+  float sm_scale;
+  void* out;
+  int64_t o_sb, o_sn, o_sh;
+  float* lse;
+  void* workspace;
+  size_t workspace_bytes;
+  int32_t num_splits;
+  int32_t path;            /* tv_path                                                       */
+} tv_attn_args;
+
+/*
+ * tree_verify_attn_workspace_size -- bytes of device workspace the call needs for these
+ * arguments (0 when one split covers every request).  Host only; the automatic split
+ * count depends on the current device's compute-unit count.  Returns 0 for arguments
+ * tree_verify_attn would reject.
+ */
+size_t tree_verify_attn_workspace_size(const tv_attn_args* a);
+
+/*
+ * tree_verify_attn -- the verification attention pass.  For every request b, node i and
+ * query head h: softmax over the allowed keys (all L prefix tokens, plus tree tokens of
+ * i's ancestors and i itself) of sm_scale * <q, k>, applied to v; lse is the natural log
+ * of the softmax denominator including its max ("Tree attention mask for draft-tree
+ * verification", "A strong answer": full step mask = all-true prefix block beside the tree
+ * mask; "Tree Verification", "Tree Attention").
+ * Enqueues one attention kernel, plus one merge kernel when a request's keys are split,
+ * on `stream`.  Errors: TV_ERR_INVALID_ARG, TV_ERR_UNSUPPORTED, TV_ERR_WORKSPACE,
+ * TV_ERR_HIP (launch failure).  B == 0 is a no-op returning TV_OK.
+ */
+tv_status tree_verify_attn(const tv_attn_args* a, hipStream_t stream);
+
+/* Static string naming a status code. */
+const char* tv_status_string(tv_status s);
+
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char* tv_last_error(void);
+
+/* TV_ABI_VERSION of the loaded library. */
+int32_t tv_abi_version(void);
+
+/* sizeof(tv_attn_args) as compiled into the library, for bindings to check their mirror. */
+size_t tv_attn_args_sizeof(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TREE_VERIFY_H */

@@ -1,0 +1,116 @@
+"""Shared machinery of the GPU parity tests: seeded inputs for both sides, a call through
+the C ABI, and the oracle's answer for any request.  The HIP side gets its tree metadata
+from the library's own builder; the oracle side from ``oracle.meta``; the two agree
+bit-exactly (checked separately)."""
+import numpy as np
+
+import tree_attention_draft_amd as tv
+from oracle import attn as oattn
+from oracle import meta as ometa
+from tree_attention_draft_amd import workloads
+
+TOL = {"bf16": 2e-2, "f32": 1e-5}
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+class Case:
+    """One batch: prefix lengths, per-request trees (rank paths or explicit parent arrays),
+    head shape, dtype, layout."""
+
+    def __init__(self, name, prefix_lens, trees=None, parents=None, Hq=32, Hkv=8, D=128,
+                 dtype="bf16", seed=1000, k_scale=False, page_size=0, page_seed=3000):
+        self.name = name
+        self.L = np.asarray(prefix_lens, np.int32)
+        self.B = len(self.L)
+        self.Hq, self.Hkv, self.D, self.dtype = Hq, Hkv, D, dtype
+        if parents is not None:
+            self.parent_gpu = [list(p) for p in parents]
+            self.parent_oracle = [list(p) for p in parents]
+        else:
+            per_request = bool(trees) and isinstance(trees[0], list)
+            if not per_request:
+                trees = [list(trees or [])] * self.B
+            self.parent_gpu = [tv.tree_meta_build(t, 0)["parent"].tolist() for t in trees]
+            self.parent_oracle = [ometa.build_from_paths(t, 0)["parent"] for t in trees]
+        self.N = len(self.parent_gpu[0])
+        assert all(len(p) == self.N for p in self.parent_gpu)
+        self.page_size = page_size
+        say(name, f"B={self.B} N={self.N} Hq={Hq} Hkv={Hkv} D={D} {dtype} "
+            f"L=[{self.L.min() if self.B else 0},{self.L.max() if self.B else 0}] "
+            f"paged={page_size} seed={seed}")
+        self.host = workloads.build_batch(seed, self.L, self.N, Hq, Hkv, D, dtype,
+                                          k_scale=k_scale, page_size=page_size,
+                                          page_seed=page_seed)
+        self._dev = None
+
+    # ------------------------------------------------------------------ device ------
+    def device(self):
+        import torch
+        if self._dev is None:
+            def up(a):
+                if a.dtype == np.uint16:
+                    return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+                return torch.from_numpy(a).cuda()
+            d = {"q": up(self.host["q"]), "k": up(self.host["k"]), "v": up(self.host["v"]),
+                 "prefix_len": torch.from_numpy(self.L).cuda(),
+                 "parent": torch.tensor(np.array(self.parent_gpu, np.int32)).cuda()}
+            if self.page_size:
+                d["page_table"] = torch.from_numpy(self.host["page_table"]).cuda()
+            self._dev = d
+        return self._dev
+
+    def run(self, **kw):
+        """Call tree_verify_attn; returns (out, lse) as float64 numpy arrays."""
+        import torch
+        d = self.device()
+        kw.setdefault("max_prefix_len", int(self.L.max()) if self.B else 0)
+        if self.page_size:
+            kw.setdefault("page_table", d["page_table"])
+            kw.setdefault("page_size", self.page_size)
+        parent = kw.pop("parent", d["parent"])
+        say(self.name, "tree_verify_attn", {k: v for k, v in kw.items()
+                                            if k in ("num_splits", "path", "max_prefix_len")})
+        out, lse = tv.tree_verify_attn(d["q"], d["k"], d["v"], parent, d["prefix_len"], **kw)
+        torch.cuda.synchronize()
+        return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+    # ------------------------------------------------------------------ oracle ------
+    def _decode(self, a):
+        if self.dtype == "bf16":
+            return oattn.bf16_bits_to_f64(a)
+        return np.asarray(a, np.float64)
+
+    def request_inputs(self, b):
+        L = int(self.L[b])
+        T = L + self.N
+        q = self._decode(self.host["q"][b])
+        if self.page_size:
+            kb = oattn.gather_paged(self.host["k"], self.host["page_table"][b], self.page_size, T)
+            vb = oattn.gather_paged(self.host["v"], self.host["page_table"][b], self.page_size, T)
+        else:
+            kb = self.host["k"][b, :T]
+            vb = self.host["v"][b, :T]
+        return q, self._decode(kb), self._decode(vb)
+
+    def oracle(self, b):
+        q, k, v = self.request_inputs(b)
+        return oattn.tree_attention_request(q, k, v, self.parent_oracle[b], int(self.L[b]))
+
+    def check(self, out, lse, requests=None, tol=None):
+        """Max-abs error of the given outputs vs the oracle over ``requests`` (all by
+        default); asserts it is within the dtype's tolerance and returns it."""
+        tol = TOL[self.dtype] if tol is None else tol
+        reqs = range(self.B) if requests is None else requests
+        worst = 0.0
+        for b in reqs:
+            o_ref, l_ref = self.oracle(b)
+            assert np.isfinite(out[b]).all() and np.isfinite(lse[b]).all(), (self.name, b)
+            eo = float(np.abs(out[b] - o_ref).max())
+            el = float(np.abs(lse[b] - l_ref).max())
+            worst = max(worst, eo, el)
+            assert eo <= tol and el <= tol, (self.name, b, eo, el)
+        say(self.name, f"max_abs_err={worst:.3e} over requests {list(reqs)[:8]}")
+        return worst

@@ -1,0 +1,220 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared symbol, the
+host builder matches the oracle bit-exactly, and every host-side argument check returns
+its documented status without touching a device."""
+import ctypes
+import itertools
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import tree_attention_draft_amd as tv
+from oracle import meta
+from tree_attention_draft_amd import workloads
+from tree_attention_draft_amd._binding import TvAttnArgs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "tree_verify.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    L = tv.lib()
+    declared = declared_functions()
+    assert set(declared) == set(tv.EXPORTS), declared
+    nm = subprocess.run(["nm", "-D", "--defined-only", tv.LIB_PATH], capture_output=True,
+                        text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in nm.splitlines() if ln.strip()}
+    for name in declared:
+        assert name in exported, name
+        assert getattr(L, name) is not None
+
+
+def test_abi_struct_and_version():
+    L = tv.lib()
+    assert L.tv_abi_version() == 1
+    assert L.tv_attn_args_sizeof() == ctypes.sizeof(TvAttnArgs)
+    for code in range(8):
+        assert L.tv_status_string(code).decode().startswith("TV_")
+
+
+# --------------------------------------------------------------- host builder ----
+def rank_paths_from_parent(parent):
+    """Rank paths of a parent array: a child's rank is its order among its siblings."""
+    paths = [()]
+    seen = {}
+    for i in range(1, len(parent)):
+        p = parent[i]
+        r = seen.get(p, 0)
+        seen[p] = r + 1
+        paths.append(paths[p] + (r,))
+    return paths[1:]
+
+
+def assert_same(paths, L):
+    ref = meta.build_from_paths(paths, L)
+    got = tv.tree_meta_build(paths, L)
+    assert got["parent"].tolist() == ref["parent"]
+    assert got["depth"].tolist() == ref["depth"]
+    assert got["pos"].tolist() == ref["pos"]
+    assert [int(x) for x in got["bitmask"]] == ref["bitmask"]
+
+
+def test_builder_worked_example_chain_empty():
+    assert_same(list(workloads.TEN_NODE_PATHS), 16)
+    assert_same(workloads.chain_paths(5), 2048)
+    assert_same([], 7)
+    got = tv.tree_meta_build([], 7)
+    assert got["parent"].tolist() == [-1] and got["bitmask"].tolist() == [1]
+
+
+def test_builder_all_trees_up_to_6_nodes():
+    for n in range(1, 7):
+        for choice in itertools.product(*[range(i) for i in range(1, n)]):
+            parent = [-1] + list(choice)
+            assert_same(rank_paths_from_parent(parent), 3)
+
+
+def test_builder_random_workload_trees_and_shuffles():
+    rng = np.random.Generator(np.random.PCG64(21))
+    for name in ("ragged64_n33", "wide32_n64", "long_paged_n33"):
+        spec = workloads.WORKLOADS[name]
+        trees, _ = workloads.trees_for(spec)
+        for paths in trees:
+            assert_same(paths, 100)
+        # shuffled input with duplicates gives the same tree
+        p = list(trees[0])
+        shuffled = p + [p[i] for i in rng.integers(0, len(p), 5)]
+        rng.shuffle(shuffled)
+        ref = tv.tree_meta_build(p, 0)
+        got = tv.tree_meta_build(shuffled, 0)
+        for k in ref:
+            assert np.array_equal(ref[k], got[k])
+
+
+@pytest.mark.parametrize("paths", [[(0, 0)], [(1,), (0, 1)], [(0,), (2, 0), (0, 0)],
+                                   [(0,), (0, 0, 0)], [(3,), (0,), (0, 5, 1), (0, 4)]])
+def test_builder_missing_parent_matches_oracle_index(paths):
+    with pytest.raises(meta.TreeError) as ref:
+        meta.build_from_paths(paths, 0)
+    with pytest.raises(tv.TreeVerifyError) as got:
+        tv.tree_meta_build(paths, 0)
+    assert got.value.name == "TV_ERR_MISSING_PARENT"
+    assert got.value.bad_path == ref.value.index
+
+
+@pytest.mark.parametrize("paths,bad", [([(0,), ()], 1), ([(0,), (0, -1)], 1)])
+def test_builder_invalid_paths(paths, bad):
+    with pytest.raises(tv.TreeVerifyError) as e:
+        tv.tree_meta_build(paths, 0)
+    assert e.value.name == "TV_ERR_INVALID_PATH" and e.value.bad_path == bad
+
+
+def test_builder_capacity():
+    paths = [(i,) for i in range(63)]
+    assert len(tv.tree_meta_build(paths, 0)["parent"]) == 64
+    with pytest.raises(tv.TreeVerifyError) as e:
+        tv.tree_meta_build(paths + [(63,)], 0, max_nodes=64)
+    assert e.value.name == "TV_ERR_CAPACITY"
+    with pytest.raises(tv.TreeVerifyError) as e:
+        tv.tree_meta_build(paths[:5], 0, max_nodes=5)
+    assert e.value.name == "TV_ERR_CAPACITY"
+    with pytest.raises(tv.TreeVerifyError) as e:
+        tv.tree_meta_build(paths + [(63,)], 0, max_nodes=100)
+    assert e.value.name == "TV_ERR_CAPACITY"
+
+
+def test_builder_bad_arguments():
+    L = tv.lib()
+    buf = np.zeros(8, np.int64)
+    out = np.zeros(64, np.int64)
+    n = ctypes.c_int32()
+    # negative num_paths, null outputs, bad offsets, negative prefix
+    assert L.tree_meta_build(None, buf.ctypes.data, -1, 0, 64, out.ctypes.data,
+                             out.ctypes.data, out.ctypes.data, out.ctypes.data,
+                             ctypes.byref(n), None) == 1
+    assert L.tree_meta_build(None, buf.ctypes.data, 0, 0, 64, None, None, None, None,
+                             None, None) == 1
+    offs = np.array([0, 2, 1], np.int64)
+    ranks = np.zeros(4, np.int32)
+    assert L.tree_meta_build(ranks.ctypes.data, offs.ctypes.data, 2, 0, 64, out.ctypes.data,
+                             out.ctypes.data, out.ctypes.data, out.ctypes.data,
+                             ctypes.byref(n), None) == 1
+    offs = np.array([0, 1], np.int64)
+    assert L.tree_meta_build(ranks.ctypes.data, offs.ctypes.data, 1, -5, 64,
+                             out.ctypes.data, out.ctypes.data, out.ctypes.data,
+                             out.ctypes.data, ctypes.byref(n), None) == 1
+
+
+# --------------------------------------------------------------- attn validation -
+def base_args(**kw):
+    a = TvAttnArgs()
+    a.dtype, a.B, a.N, a.Hq, a.Hkv, a.D = 0, 2, 10, 32, 8, 128
+    fake = 1 << 20  # aligned, never dereferenced: validation fails before any launch
+    a.q = a.k = a.v = a.out = fake
+    a.parent = a.prefix_len = fake
+    a.q_sb, a.q_sn, a.q_sh = 10 * 32 * 128, 32 * 128, 128
+    a.kv_sb, a.kv_st, a.kv_sh = 100 * 8 * 128, 8 * 128, 128
+    a.o_sb, a.o_sn, a.o_sh = a.q_sb, a.q_sn, a.q_sh
+    a.parent_sb = 10
+    a.max_prefix_len = 64
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=0), 1), (dict(N=65), 1), (dict(Hq=30), 1), (dict(Hkv=0), 1),
+    (dict(D=96), 5), (dict(dtype=7), 1), (dict(B=-1), 1), (dict(q=None), 1),
+    (dict(parent=None), 1), (dict(prefix_len=None), 1), (dict(out=None), 1),
+    (dict(q_sn=100), 1), (dict(kv_st=-8), 1), (dict(k=(1 << 20) + 8), 1),
+    (dict(parent_sb=3), 1), (dict(max_prefix_len=-1), 1), (dict(sm_scale=-1.0), 1),
+    (dict(sm_scale=float("inf")), 1), (dict(num_splits=-2), 1), (dict(path=9), 1),
+    (dict(path=2, dtype=1), 5), (dict(kv_layout=1), 1),
+    (dict(kv_layout=1, page_table=1 << 20, page_size=16, pages_per_seq=4), 1),
+    (dict(kv_layout=3), 1),
+])
+def test_attn_argument_checks(kw, status):
+    a = base_args(**kw)
+    L = tv.lib()
+    assert L.tree_verify_attn(ctypes.byref(a), None) == status
+    assert L.tree_verify_attn_workspace_size(ctypes.byref(a)) == 0
+    assert L.tv_last_error().decode() != ""
+
+
+def test_attn_empty_batch_is_noop():
+    a = base_args(B=0, q=None, k=None, v=None, out=None, parent=None, prefix_len=None)
+    assert tv.lib().tree_verify_attn(ctypes.byref(a), None) == 0
+
+
+def test_workspace_missing_is_rejected_before_launch():
+    # B=1, long prefix: the plan splits keys, so a workspace is required
+    a = base_args(B=1, max_prefix_len=32768, num_splits=8)
+    need = tv.lib().tree_verify_attn_workspace_size(ctypes.byref(a))
+    R = 10 * 4
+    assert need == 1 * 8 * 8 * R * (128 + 1) * 4
+    assert tv.lib().tree_verify_attn(ctypes.byref(a), None) == 6
+    a.workspace, a.workspace_bytes = 1 << 20, need - 4
+    assert tv.lib().tree_verify_attn(ctypes.byref(a), None) == 6
+
+
+def test_single_split_needs_no_workspace():
+    a = base_args(num_splits=1)
+    assert tv.lib().tree_verify_attn_workspace_size(ctypes.byref(a)) == 0
+
+
+def test_meta_from_parent_argument_checks():
+    L = tv.lib()
+    assert L.tree_meta_from_parent(1 << 20, 0, 4, 0, None, None, None, None, None) == 1
+    assert L.tree_meta_from_parent(1 << 20, 0, 4, 65, None, None, None, None, None) == 1
+    assert L.tree_meta_from_parent(1 << 20, 5, 4, 10, None, None, None, None, None) == 1
+    assert L.tree_meta_from_parent(None, 0, 4, 10, None, None, None, None, None) == 1
+    assert L.tree_meta_from_parent(None, 0, 0, 10, None, None, None, None, None) == 0

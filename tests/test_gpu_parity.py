@@ -1,0 +1,263 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle, element by element.
+
+Tolerances: max-abs 2e-2 on outputs and LSE for bf16 inputs (fp32 accumulation), 1e-5
+for fp32 inputs; tree metadata bit-exact.  Small cases are checked in full; the full-size
+workloads in the launch configuration the benchmark times are checked on sampled
+requests (every node and head of each sampled request).
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+import tree_attention_draft_amd as tv  # noqa: E402
+from oracle import meta as ometa  # noqa: E402
+from tree_attention_draft_amd import workloads  # noqa: E402
+
+from gpu_cases import Case, say  # noqa: E402
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+TEN = list(workloads.TEN_NODE_PATHS)
+
+
+def random_trees(seed, B, n, cap):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    paths, creation = [], []
+    for _ in range(B):
+        p, c = workloads.random_tree(rng, n, cap)
+        paths.append(p)
+        creation.append(c)
+    return paths, creation
+
+
+# ------------------------------------------------------------------ metadata ----------
+def test_meta_from_parent_bit_exact():
+    cases = []
+    paths, creation = random_trees(2003, 64, 33, 8)
+    cases.append(("random33", [ometa.build_from_paths(p, 0)["parent"] for p in paths]))
+    cases.append(("creation_order33", creation))
+    paths64, _ = random_trees(2004, 32, 64, 10)
+    cases.append(("random64", [ometa.build_from_paths(p, 0)["parent"] for p in paths64]))
+    cases.append(("tree10", [ometa.build_from_paths(TEN, 0)["parent"]] * 3))
+    cases.append(("chain5", [[-1, 0, 1, 2, 3]] * 2))
+    cases.append(("empty", [[-1]] * 5))
+    for name, parents in cases:
+        say("meta_from_parent", name)
+        P = torch.tensor(np.array(parents, np.int32)).cuda()
+        L = torch.arange(P.shape[0], dtype=torch.int32).cuda() * 100 + 7
+        depth, bitmask, pos = tv.tree_meta_from_parent(P, L)
+        depth, bitmask, pos = depth.cpu().numpy(), bitmask.cpu().numpy(), pos.cpu().numpy()
+        for b, par in enumerate(parents):
+            ref = ometa.meta_from_parent(par, 100 * b + 7)
+            assert depth[b].tolist() == ref["depth"]
+            assert pos[b].tolist() == ref["pos"]
+            assert [int(x) & (2 ** 64 - 1) for x in bitmask[b]] == ref["bitmask"]
+
+
+def test_meta_from_parent_shared_tree_and_invalid_nodes():
+    par = ometa.build_from_paths(TEN, 0)["parent"]
+    P = torch.tensor(par, dtype=torch.int32).cuda()
+    L = torch.tensor([5, 9, 11], dtype=torch.int32).cuda()
+    depth, bitmask, pos = tv.tree_meta_from_parent(P, L)   # one tree, 3 requests
+    for b, Lb in enumerate([5, 9, 11]):
+        ref = ometa.meta_from_parent(par, Lb)
+        assert pos[b].cpu().tolist() == ref["pos"]
+        assert [int(x) for x in bitmask[b].cpu()] == ref["bitmask"]
+    # broken conventions are flagged node by node, never read out of bounds
+    bad = torch.tensor([[-1, 0, 2, 1, 7], [3, 0, 1, 2, 3], [-1, 0, 1, -1, 3]],
+                       dtype=torch.int32).cuda()
+    depth, bitmask, pos = tv.tree_meta_from_parent(bad)
+    d = depth.cpu().tolist()
+    assert d[0] == [0, 1, -1, 2, -1]
+    assert d[1] == [-1, -1, -1, -1, -1]
+    assert d[2] == [0, 1, 2, -1, -1]
+    assert int(bitmask[0, 1]) == 0b11 and int(bitmask[0, 2]) == 0
+
+
+# ------------------------------------------------------------------ worked example ----
+@pytest.mark.parametrize("tree", ["tree10", "empty", "chain5"])
+@pytest.mark.parametrize("splits", [0, 1, 2])
+def test_single_request_fp32(tree, splits):
+    trees = {"tree10": TEN, "empty": [], "chain5": workloads.chain_paths(5)}[tree]
+    c = Case(f"{tree}_f32", [16], trees=trees, Hq=1, Hkv=1, D=64, dtype="f32", seed=1001)
+    out, lse = c.run(num_splits=splits)
+    c.check(out, lse)
+
+
+@pytest.mark.parametrize("tree", ["tree10", "chain5"])
+def test_llama8b_shape_full(tree):
+    trees = TEN if tree == "tree10" else workloads.chain_paths(5)
+    c = Case(f"llama8b_{tree}", [2048] * 8, trees=trees, seed=1002)
+    out, lse = c.run()
+    c.check(out, lse)
+
+
+# ------------------------------------------------------------------ shapes & paths ----
+@pytest.mark.parametrize("N", [1, 2, 5, 10, 16, 17, 33, 63, 64])
+def test_node_count_sweep(N):
+    paths, _ = random_trees(500 + N, 2, N, 8)
+    c = Case(f"nodes{N}", [300, 77], trees=paths, seed=1100 + N)
+    out, lse = c.run()
+    c.check(out, lse)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (32, 8), (16, 2)])
+def test_head_shapes_and_forced_paths(D, hq, hkv):
+    paths, _ = random_trees(600, 3, 12, 5)
+    c = Case(f"heads{hq}_{hkv}_D{D}", [130, 64, 1], trees=paths, Hq=hq, Hkv=hkv, D=D,
+             seed=1200 + D + hq)
+    results = {}
+    for path in ("auto", "valu", "mfma"):
+        out, lse = c.run(path=path)
+        c.check(out, lse)
+        results[path] = out
+    assert np.abs(results["valu"] - results["mfma"]).max() <= 2e-2
+
+
+@pytest.mark.parametrize("splits", [1, 2, 7, 1000])
+def test_split_invariance(splits):
+    paths, _ = random_trees(700, 3, 33, 8)
+    c = Case("splits", [1000, 999, 33], trees=paths, seed=1300)
+    out, lse = c.run(num_splits=splits)
+    c.check(out, lse)
+
+
+def test_prefix_edges_in_one_batch():
+    Ls = [0, 1, 63, 64, 65, 127, 128, 129, 5]
+    paths, _ = random_trees(800, len(Ls), 33, 8)
+    c = Case("prefix_edges", Ls, trees=paths, seed=1400)
+    for splits in (0, 1, 3):
+        out, lse = c.run(num_splits=splits)
+        c.check(out, lse)
+
+
+def test_fp32_larger_rows_valu():
+    paths, _ = random_trees(900, 2, 20, 6)
+    c = Case("f32_rows", [200, 333], trees=paths, Hq=8, Hkv=2, D=128, dtype="f32",
+             seed=1500)
+    out, lse = c.run()
+    c.check(out, lse)
+    out, lse = c.run(num_splits=4)
+    c.check(out, lse)
+
+
+# ------------------------------------------------------------------ invariants --------
+def test_non_ancestor_edits_leave_node_bit_identical():
+    par = ometa.build_from_paths(TEN, 0)["parent"]
+    c = Case("edit_nonancestor", [200, 200], parents=[par, par], seed=1600)
+    base, base_lse = c.run()
+    d = c.device()
+    node = 9
+    anc = {9, 6, 3, 1, 0}
+    k2, v2 = d["k"].clone(), d["v"].clone()
+    for j in range(len(par)):
+        if j not in anc:
+            k2[:, 200 + j] = torch.randn_like(k2[:, 200 + j].float()).to(k2.dtype) * 50
+            v2[:, 200 + j] = torch.randn_like(v2[:, 200 + j].float()).to(v2.dtype) * 50
+    out, lse = tv.tree_verify_attn(d["q"], k2, v2, d["parent"], d["prefix_len"], 200)
+    out = out.float().cpu().numpy()
+    assert np.array_equal(out[:, node], base[:, node])
+    assert np.array_equal(lse.cpu().numpy()[:, node], base_lse[:, node])
+
+
+def test_relabelling_permutes_outputs():
+    paths, creation = random_trees(1000, 2, 33, 8)
+    canon = [ometa.build_from_paths(p, 0) for p in paths]
+    c1 = Case("canonical", [400, 250], trees=paths, seed=1700)
+    out1, lse1 = c1.run()
+    c1.check(out1, lse1)
+    # same tokens stored in creation order: Q rows and tree K/V rows permuted
+    c2 = Case("creation_order", [400, 250], parents=creation, seed=1700)
+    for b in range(2):
+        index = {p: i for i, p in enumerate(canon[b]["paths"])}
+        perm = [index[p] for p in [()] + paths[b]]        # creation i -> canonical
+        L = [400, 250][b]
+        for key in ("k", "v"):
+            c2.host[key][b, L:L + 33] = c1.host[key][b, L:L + 33][perm]
+        c2.host["q"][b] = c1.host["q"][b][perm]
+    out2, lse2 = c2.run()
+    c2.check(out2, lse2)
+    for b in range(2):
+        index = {p: i for i, p in enumerate(canon[b]["paths"])}
+        perm = [index[p] for p in [()] + paths[b]]
+        assert np.abs(out2[b] - out1[b][perm]).max() <= 2e-2
+
+
+def test_shared_tree_strided_tensors_and_no_lse():
+    par = ometa.build_from_paths(TEN, 0)["parent"]
+    c = Case("shared_strided", [300, 301, 302], parents=[par] * 3, seed=1800)
+    d = c.device()
+    big_q = torch.zeros((3, 10, 40, 128), dtype=torch.bfloat16, device="cuda")
+    big_q[:, :, 4:36] = d["q"]
+    q_view = big_q[:, :, 4:36]                      # non-contiguous head stride window
+    out_big = torch.full((3, 12, 32, 136), float("nan"), dtype=torch.bfloat16, device="cuda")
+    out_view = out_big[:, 1:11, :, :128]
+    shared = torch.tensor(par, dtype=torch.int32, device="cuda")
+    tv.tree_verify_attn(q_view, d["k"], d["v"], shared, d["prefix_len"], 302, out=out_view)
+    ref_out, ref_lse = c.run()
+    got = out_view.float().cpu().numpy()
+    assert np.array_equal(got, ref_out)
+    assert torch.isnan(out_big[:, 0].float()).all() and torch.isnan(out_big[:, 11].float()).all()
+    # lse may be omitted (NULL)
+    a = tv.make_args(d["q"], d["k"], d["v"], d["parent"], d["prefix_len"], 302,
+                     out=torch.empty_like(d["q"]), num_splits=1)
+    import ctypes
+    st = tv.lib().tree_verify_attn(ctypes.byref(a),
+                                   ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0
+
+
+def test_empty_batch_noop():
+    q = torch.empty((0, 5, 32, 128), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty((0, 10, 8, 128), dtype=torch.bfloat16, device="cuda")
+    par = torch.empty((0, 5), dtype=torch.int32, device="cuda")
+    pl = torch.empty((0,), dtype=torch.int32, device="cuda")
+    out, lse = tv.tree_verify_attn(q, k, k, par, pl, 0)
+    assert out.shape == (0, 5, 32, 128)
+
+
+# ------------------------------------------------------------------ workloads ---------
+def test_ragged_small_full():
+    spec = workloads.WORKLOADS["ragged64_n33"]
+    trees, _ = workloads.trees_for(spec)
+    L = workloads.prefix_lengths(spec)[:6] // 4
+    c = Case("ragged_small", L, trees=trees[:6], seed=1003)
+    out, lse = c.run()
+    c.check(out, lse)
+
+
+def _sampled(B):
+    return sorted(b for b in {0, 1, B // 2, B - 1} if b < B)
+
+
+@pytest.mark.parametrize("name", ["ragged64_n33", "b64_l4096_n33", "wide32_n64"])
+def test_full_size_workloads_sampled(name):
+    spec = workloads.WORKLOADS[name]
+    trees, _ = workloads.trees_for(spec)
+    L = workloads.prefix_lengths(spec)
+    c = Case(name, L, trees=trees, Hq=spec["Hq"], Hkv=spec["Hkv"], D=spec["D"],
+             seed=1000 + spec["k"], k_scale=spec.get("k_scale", False))
+    out, lse = c.run()
+    c.check(out, lse, requests=_sampled(c.B))
+
+
+@pytest.mark.parametrize("B", [1, 16])
+def test_long_context_paged_sampled(B):
+    spec = workloads.WORKLOADS["long_paged_n33"]
+    trees, _ = workloads.trees_for(spec, batch=B)
+    L = workloads.prefix_lengths(spec, batch=B)
+    c = Case(f"long_paged_B{B}", L, trees=trees, seed=1005, page_size=16, page_seed=3005)
+    out, lse = c.run()
+    c.check(out, lse, requests=_sampled(B)[:3])
+
+
+def test_paged_small_full_with_splits():
+    spec = workloads.WORKLOADS["long_paged_n33"]
+    trees, _ = workloads.trees_for(spec, batch=4)
+    c = Case("paged_small", [1000, 17, 400, 2048], trees=trees, seed=1905, page_size=16,
+             page_seed=3905)
+    for splits in (0, 1, 5):
+        out, lse = c.run(num_splits=splits)
+        c.check(out, lse)

@@ -1,0 +1,10 @@
+"""Tree-verification attention for MI355X (gfx950).
+
+The work runs in ``libtreeverify.so`` (hand-written HIP kernels plus a host C++ tree
+builder) behind the C ABI declared in ``include/tree_verify.h``; this package is its thin
+Python binding plus the seeded workload generators used by the tests and the benchmark.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTS, LIB_PATH, MAX_NODES, TreeVerifyError, TvAttnArgs, lib, make_args,
+    tree_meta_build, tree_meta_from_parent, tree_verify_attn,
+    tree_verify_attn_workspace_size)

@@ -1,0 +1,255 @@
+"""ctypes binding of libtreeverify.so (see include/tree_verify.h).
+
+Marshalling only: every step of the path runs in the library's HIP kernels or its host C++
+builder.  PyTorch supplies device memory and the current stream.  If the shared library
+is missing this module raises on first use -- there is no fallback.
+"""
+import ctypes
+import math
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtreeverify.so")
+
+TV_OK = 0
+STATUS_NAMES = {0: "TV_OK", 1: "TV_ERR_INVALID_ARG", 2: "TV_ERR_INVALID_PATH",
+                3: "TV_ERR_MISSING_PARENT", 4: "TV_ERR_CAPACITY", 5: "TV_ERR_UNSUPPORTED",
+                6: "TV_ERR_WORKSPACE", 7: "TV_ERR_HIP"}
+TV_BF16, TV_F32 = 0, 1
+TV_KV_CONTIGUOUS, TV_KV_PAGED = 0, 1
+PATHS = {"auto": 0, "valu": 1, "mfma": 2}
+MAX_NODES = 64
+
+# Every symbol include/tree_verify.h declares.
+EXPORTS = ["tree_meta_build", "tree_meta_from_parent", "tree_verify_attn_workspace_size",
+           "tree_verify_attn", "tv_status_string", "tv_last_error", "tv_abi_version",
+           "tv_attn_args_sizeof"]
+
+
+class TreeVerifyError(RuntimeError):
+    def __init__(self, status, detail, bad_path=-1):
+        self.status = status
+        self.name = STATUS_NAMES.get(status, str(status))
+        self.bad_path = bad_path
+        super().__init__(f"{self.name}: {detail}" + (
+            f" (input path {bad_path})" if bad_path >= 0 else ""))
+
+
+class TvAttnArgs(ctypes.Structure):
+    """Mirror of ``tv_attn_args`` (field order and types must match the header)."""
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("B", ctypes.c_int32), ("N", ctypes.c_int32),
+        ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("q", ctypes.c_void_p),
+        ("q_sb", ctypes.c_int64), ("q_sn", ctypes.c_int64), ("q_sh", ctypes.c_int64),
+        ("kv_layout", ctypes.c_int32), ("page_size", ctypes.c_int32),
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("kv_sb", ctypes.c_int64), ("kv_st", ctypes.c_int64), ("kv_sh", ctypes.c_int64),
+        ("page_table", ctypes.c_void_p),
+        ("pages_per_seq", ctypes.c_int32), ("parent_sb", ctypes.c_int32),
+        ("parent", ctypes.c_void_p), ("prefix_len", ctypes.c_void_p),
+        ("max_prefix_len", ctypes.c_int32), ("sm_scale", ctypes.c_float),
+        ("out", ctypes.c_void_p),
+        ("o_sb", ctypes.c_int64), ("o_sn", ctypes.c_int64), ("o_sh", ctypes.c_int64),
+        ("lse", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("num_splits", ctypes.c_int32), ("path", ctypes.c_int32),
+    ]
+
+
+_LIB = None
+
+
+def lib():
+    """The loaded library (loads it on first call; raises if it was never built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m tree_attention_draft_amd.build` "
+            "(the HIP library is required; there is no CPU fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    L.tree_meta_build.restype = i32
+    L.tree_meta_build.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+    L.tree_meta_from_parent.restype = i32
+    L.tree_meta_from_parent.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp]
+    L.tree_verify_attn_workspace_size.restype = ctypes.c_size_t
+    L.tree_verify_attn_workspace_size.argtypes = [ctypes.POINTER(TvAttnArgs)]
+    L.tree_verify_attn.restype = i32
+    L.tree_verify_attn.argtypes = [ctypes.POINTER(TvAttnArgs), vp]
+    L.tv_status_string.restype = ctypes.c_char_p
+    L.tv_status_string.argtypes = [i32]
+    L.tv_last_error.restype = ctypes.c_char_p
+    L.tv_last_error.argtypes = []
+    L.tv_abi_version.restype = i32
+    L.tv_attn_args_sizeof.restype = ctypes.c_size_t
+    _LIB = L
+    return L
+
+
+def _check(status, bad_path=-1):
+    if status != TV_OK:
+        raise TreeVerifyError(status, lib().tv_last_error().decode(), bad_path)
+
+
+# ------------------------------------------------------------------- host builder ----
+def tree_meta_build(paths, prefix_len, max_nodes=MAX_NODES):
+    """Rank paths -> dict of numpy arrays ``parent``, ``depth``, ``bitmask`` (uint64),
+    ``pos`` (length N), built by the library's host C++ builder."""
+    offs = [0]
+    flat = []
+    for p in paths:
+        flat.extend(int(x) for x in p)
+        offs.append(len(flat))
+    ranks = np.asarray(flat if flat else [0], dtype=np.int32)
+    path_off = np.asarray(offs, dtype=np.int64)
+    cap = int(max_nodes)
+    parent = np.empty(cap, np.int32)
+    depth = np.empty(cap, np.int32)
+    bitmask = np.empty(cap, np.uint64)
+    pos = np.empty(cap, np.int32)
+    n = ctypes.c_int32(0)
+    bad = ctypes.c_int32(-1)
+    st = lib().tree_meta_build(
+        ranks.ctypes.data, path_off.ctypes.data, len(paths), int(prefix_len), cap,
+        parent.ctypes.data, depth.ctypes.data, bitmask.ctypes.data, pos.ctypes.data,
+        ctypes.byref(n), ctypes.byref(bad))
+    _check(st, bad.value)
+    k = n.value
+    return {"parent": parent[:k].copy(), "depth": depth[:k].copy(),
+            "bitmask": bitmask[:k].copy(), "pos": pos[:k].copy()}
+
+
+# ------------------------------------------------------------------- device side -----
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _require_cuda(*tensors):
+    for t in tensors:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tree-verify device entry points take GPU tensors")
+
+
+def tree_meta_from_parent(parent, prefix_len=None, batch=None, depth=None, bitmask=None,
+                          pos=None, stream=None):
+    """Device metadata from int32 parent arrays ``[B, N]`` (or ``[N]`` shared by ``batch``
+    requests).  Returns ``(depth, bitmask, pos)`` as [B, N] tensors (int32, int64 holding
+    the uint64 bit pattern, int32)."""
+    torch = _torch()
+    _require_cuda(parent, prefix_len)
+    if parent.dtype != torch.int32:
+        raise ValueError("parent must be int32")
+    if parent.dim() == 1:
+        if batch is None:
+            batch = prefix_len.shape[0] if prefix_len is not None else 1
+        B, N, psb = int(batch), parent.shape[0], 0
+    else:
+        B, N = parent.shape
+        psb = parent.stride(0)
+        if parent.stride(1) != 1:
+            raise ValueError("parent rows must be contiguous")
+    dev = parent.device
+    depth = torch.empty((B, N), dtype=torch.int32, device=dev) if depth is None else depth
+    bitmask = torch.empty((B, N), dtype=torch.int64, device=dev) if bitmask is None else bitmask
+    pos = torch.empty((B, N), dtype=torch.int32, device=dev) if pos is None else pos
+    st = lib().tree_meta_from_parent(
+        parent.data_ptr(), psb, B, N,
+        prefix_len.data_ptr() if prefix_len is not None else None,
+        depth.data_ptr(), bitmask.data_ptr(), pos.data_ptr(), _stream(stream))
+    _check(st)
+    return depth, bitmask, pos
+
+
+def make_args(q, k, v, parent, prefix_len, max_prefix_len, page_table=None, page_size=0,
+              sm_scale=0.0, out=None, lse=None, workspace=None, num_splits=0, path="auto"):
+    """Fill a TvAttnArgs from torch tensors (no allocation, no checks beyond shapes)."""
+    torch = _torch()
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    a = TvAttnArgs()
+    if q.dtype == torch.bfloat16:
+        a.dtype = TV_BF16
+    elif q.dtype == torch.float32:
+        a.dtype = TV_F32
+    else:
+        raise ValueError("q must be bfloat16 or float32")
+    a.B, a.N, a.Hq, a.Hkv, a.D = B, N, Hq, Hkv, D
+    a.q = q.data_ptr()
+    a.q_sb, a.q_sn, a.q_sh = q.stride(0), q.stride(1), q.stride(2)
+    a.k, a.v = k.data_ptr(), v.data_ptr()
+    if k.stride() != v.stride():
+        raise ValueError("k and v must share strides")
+    a.kv_sb, a.kv_st, a.kv_sh = k.stride(0), k.stride(1), k.stride(2)
+    if page_table is not None:
+        a.kv_layout = TV_KV_PAGED
+        a.page_size = int(page_size) if page_size else k.shape[1]
+        a.page_table = page_table.data_ptr()
+        a.pages_per_seq = page_table.shape[1]
+    else:
+        a.kv_layout = TV_KV_CONTIGUOUS
+    if parent.dim() == 1:
+        a.parent_sb = 0
+    else:
+        a.parent_sb = parent.stride(0)
+    a.parent = parent.data_ptr()
+    a.prefix_len = prefix_len.data_ptr()
+    a.max_prefix_len = int(max_prefix_len)
+    a.sm_scale = float(sm_scale)
+    if out is not None:
+        a.out = out.data_ptr()
+        a.o_sb, a.o_sn, a.o_sh = out.stride(0), out.stride(1), out.stride(2)
+    a.lse = lse.data_ptr() if lse is not None else None
+    if workspace is not None:
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    a.num_splits = int(num_splits)
+    a.path = PATHS[path] if isinstance(path, str) else int(path)
+    return a
+
+
+def tree_verify_attn_workspace_size(q, k, v, parent, prefix_len, max_prefix_len, **kw):
+    a = make_args(q, k, v, parent, prefix_len, max_prefix_len, **kw)
+    return int(lib().tree_verify_attn_workspace_size(ctypes.byref(a)))
+
+
+def tree_verify_attn(q, k, v, parent, prefix_len, max_prefix_len, *, page_table=None,
+                     page_size=0, sm_scale=0.0, out=None, lse=None, workspace=None,
+                     num_splits=0, path="auto", stream=None):
+    """Tree-verification attention.  q [B, N, Hq, D]; k, v [B, S, Hkv, D] (contiguous) or
+    [pages, page_size, Hkv, D] with ``page_table`` [B, pages_per_seq]; parent int32 [B, N]
+    or [N]; prefix_len int32 [B].  Returns ``(out, lse)``; ``lse`` is the natural-log
+    log-sum-exp per (request, node, query head)."""
+    torch = _torch()
+    _require_cuda(q, k, v, parent, prefix_len, page_table, out, lse, workspace)
+    B, N, Hq, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, N, Hq), dtype=torch.float32, device=q.device)
+    a = make_args(q, k, v, parent, prefix_len, max_prefix_len, page_table=page_table,
+                  page_size=page_size, sm_scale=sm_scale, out=out, lse=lse,
+                  workspace=workspace, num_splits=num_splits, path=path)
+    need = int(lib().tree_verify_attn_workspace_size(ctypes.byref(a)))
+    if need > 0 and (workspace is None or a.workspace_bytes < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = need
+    st = lib().tree_verify_attn(ctypes.byref(a), _stream(stream))
+    _check(st)
+    return out, lse
+
+
+def default_scale(D):
+    return 1.0 / math.sqrt(D)

@@ -1,0 +1,273 @@
+// C-ABI host glue of libtreeverify: argument checks, split planning, kernel dispatch.
+// Nothing here allocates device memory or synchronises; every device action is a kernel
+// launch on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "tree_verify.h"
+#include "tv_internal.h"
+
+namespace tv {
+
+namespace {
+thread_local char g_last_error[256] = "";
+
+struct Plan {
+  bool mfma = false;
+  MfmaShape shape{1, 1};
+  int row_chunks = 1;
+  int rows_per_wg = 16;
+  int splits = 1;
+  int chunk = kKeysPerTile;
+  size_t ws_o_bytes = 0;
+  size_t ws_bytes = 0;
+};
+
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0) {
+    (void)hipGetLastError();
+    n = 256;
+  }
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+MfmaShape pick_mfma_shape(int qt, int* row_chunks) {
+  *row_chunks = 1;
+  if (qt <= 4) return MfmaShape{1, qt};
+  if (qt <= 8) return MfmaShape{2, (qt + 1) / 2};
+  if (qt <= 12) return MfmaShape{3, (qt + 2) / 3};
+  if (qt <= 16) return MfmaShape{4, (qt + 3) / 4};
+  *row_chunks = (qt + 31) / 32;
+  return MfmaShape{4, 8};
+}
+
+tv_status check_args(const tv_attn_args* a) {
+  if (!a) return fail(TV_ERR_INVALID_ARG, "args is null");
+  if (a->dtype != TV_BF16 && a->dtype != TV_F32) return fail(TV_ERR_INVALID_ARG, "bad dtype");
+  if (a->B < 0) return fail(TV_ERR_INVALID_ARG, "B < 0");
+  if (a->N < 1 || a->N > TV_MAX_NODES) return fail(TV_ERR_INVALID_ARG, "N outside 1..64");
+  if (a->Hq < 1 || a->Hkv < 1 || a->Hq % a->Hkv != 0)
+    return fail(TV_ERR_INVALID_ARG, "need Hq >= 1, Hkv >= 1 and Hq % Hkv == 0");
+  if (a->D != 64 && a->D != 128) return fail(TV_ERR_UNSUPPORTED, "D must be 64 or 128");
+  if (a->kv_layout != TV_KV_CONTIGUOUS && a->kv_layout != TV_KV_PAGED)
+    return fail(TV_ERR_INVALID_ARG, "bad kv_layout");
+  if (a->path != TV_PATH_AUTO && a->path != TV_PATH_VALU && a->path != TV_PATH_MFMA)
+    return fail(TV_ERR_INVALID_ARG, "bad path");
+  if (a->path == TV_PATH_MFMA && a->dtype != TV_BF16)
+    return fail(TV_ERR_UNSUPPORTED, "the MFMA path takes bf16 inputs");
+  if (a->num_splits < 0) return fail(TV_ERR_INVALID_ARG, "num_splits < 0");
+  if (a->max_prefix_len < 0 || a->max_prefix_len > INT32_MAX - 2 * TV_MAX_NODES - 64)
+    return fail(TV_ERR_INVALID_ARG, "max_prefix_len out of range");
+  if (!(a->sm_scale >= 0.f) || !std::isfinite(a->sm_scale))
+    return fail(TV_ERR_INVALID_ARG, "sm_scale must be finite and >= 0");
+  if (a->B == 0) return TV_OK;
+  if (!a->q || !a->k || !a->v || !a->parent || !a->prefix_len || !a->out)
+    return fail(TV_ERR_INVALID_ARG, "null q, k, v, parent, prefix_len or out");
+  if (a->parent_sb < 0) return fail(TV_ERR_INVALID_ARG, "parent_sb < 0");
+  if (a->parent_sb > 0 && a->parent_sb < a->N)
+    return fail(TV_ERR_INVALID_ARG, "parent_sb must be 0 or >= N");
+  const int64_t vec = a->dtype == TV_BF16 ? 8 : 4;  // elements per 16 bytes
+  const int64_t strides[] = {a->q_sb, a->q_sn, a->q_sh, a->kv_sb, a->kv_st, a->kv_sh,
+                             a->o_sb, a->o_sn, a->o_sh};
+  for (int64_t s : strides) {
+    if (s < 0 || s % vec != 0)
+      return fail(TV_ERR_INVALID_ARG, "strides must be >= 0 and multiples of 16 bytes");
+  }
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->out))
+    return fail(TV_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+  if (a->kv_layout == TV_KV_PAGED) {
+    if (!a->page_table || a->page_size < 1 || a->pages_per_seq < 1)
+      return fail(TV_ERR_INVALID_ARG, "paged KV needs page_table, page_size, pages_per_seq");
+    const int64_t need = ((int64_t)a->max_prefix_len + a->N + a->page_size - 1) / a->page_size;
+    if (a->pages_per_seq < need)
+      return fail(TV_ERR_INVALID_ARG, "pages_per_seq too small for max_prefix_len + N");
+  }
+  if (a->B > 65535) return fail(TV_ERR_UNSUPPORTED, "B > 65535");
+  return TV_OK;
+}
+
+tv_status make_plan(const tv_attn_args* a, Plan* pl) {
+  const int g = a->Hq / a->Hkv;
+  const int R = a->N * g;
+  const bool bf16 = a->dtype == TV_BF16;
+  pl->mfma = a->path == TV_PATH_MFMA || (a->path == TV_PATH_AUTO && bf16 && R >= 16);
+  if (pl->mfma) {
+    const int qt = (R + 15) / 16;
+    pl->shape = pick_mfma_shape(qt, &pl->row_chunks);
+    pl->rows_per_wg = pl->shape.tpw * pl->shape.nw * 16;
+  } else {
+    pl->rows_per_wg = kValuRowsPerWg;
+    pl->row_chunks = (R + kValuRowsPerWg - 1) / kValuRowsPerWg;
+  }
+  if ((int64_t)a->Hkv * pl->row_chunks > 65535)
+    return fail(TV_ERR_UNSUPPORTED, "Hkv * row chunks > 65535");
+  const int64_t tmax = (int64_t)a->max_prefix_len + a->N;
+  const int64_t tiles = (tmax + kKeysPerTile - 1) / kKeysPerTile;
+  const int64_t pairs = (int64_t)a->B * a->Hkv * pl->row_chunks;
+  int64_t S;
+  if (a->num_splits > 0) {
+    S = std::min<int64_t>(a->num_splits, tiles);
+  } else {
+    const int64_t target = 2 * (int64_t)device_cu_count();
+    S = pairs >= target ? 1 : std::min<int64_t>(tiles, (target + pairs - 1) / pairs);
+  }
+  S = std::max<int64_t>(S, 1);
+  const int64_t chunk_tiles = (tiles + S - 1) / S;
+  S = (tiles + chunk_tiles - 1) / chunk_tiles;
+  pl->splits = (int)S;
+  pl->chunk = (int)(chunk_tiles * kKeysPerTile);
+  if (S > 1) {
+    const size_t rows = (size_t)a->B * a->Hkv * S * R;
+    pl->ws_o_bytes = rows * a->D * sizeof(float);
+    pl->ws_bytes = pl->ws_o_bytes + rows * sizeof(float);
+  }
+  return TV_OK;
+}
+
+AttnParams make_params(const tv_attn_args* a, const Plan& pl) {
+  AttnParams p{};
+  p.q = a->q;
+  p.q_sb = a->q_sb;
+  p.q_sn = a->q_sn;
+  p.q_sh = a->q_sh;
+  p.k = a->k;
+  p.v = a->v;
+  p.kv_sb = a->kv_sb;
+  p.kv_st = a->kv_st;
+  p.kv_sh = a->kv_sh;
+  p.paged = a->kv_layout == TV_KV_PAGED;
+  p.page_table = a->page_table;
+  p.page_size = p.paged ? a->page_size : 1;
+  p.pages_per_seq = a->pages_per_seq;
+  p.page_shift = -1;
+  if (p.paged && (a->page_size & (a->page_size - 1)) == 0) {
+    int sh = 0;
+    while ((1 << sh) < a->page_size) ++sh;
+    p.page_shift = sh;
+  }
+  p.parent = a->parent;
+  p.parent_sb = a->parent_sb;
+  p.prefix_len = a->prefix_len;
+  p.max_prefix_len = a->max_prefix_len;
+  p.out = a->out;
+  p.o_sb = a->o_sb;
+  p.o_sn = a->o_sn;
+  p.o_sh = a->o_sh;
+  p.lse = a->lse;
+  p.B = a->B;
+  p.N = a->N;
+  p.Hq = a->Hq;
+  p.Hkv = a->Hkv;
+  p.g = a->Hq / a->Hkv;
+  p.R = a->N * p.g;
+  p.num_splits = pl.splits;
+  p.chunk = pl.chunk;
+  p.row_chunks = pl.row_chunks;
+  p.rows_per_wg = pl.rows_per_wg;
+  const float scale = a->sm_scale > 0.f ? a->sm_scale : 1.0f / std::sqrt((float)a->D);
+  p.scale_log2 = scale * 1.4426950408889634f;
+  if (pl.splits > 1) {
+    p.ws_o = static_cast<float*>(a->workspace);
+    p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + pl.ws_o_bytes);
+  }
+  return p;
+}
+
+}  // namespace
+
+tv_status fail(tv_status s, const char* detail) {
+  std::strncpy(g_last_error, detail ? detail : "", sizeof(g_last_error) - 1);
+  g_last_error[sizeof(g_last_error) - 1] = '\0';
+  return s;
+}
+
+}  // namespace tv
+
+using namespace tv;
+
+extern "C" size_t tree_verify_attn_workspace_size(const tv_attn_args* a) {
+  if (check_args(a) != TV_OK || a->B == 0) return 0;
+  Plan pl;
+  if (make_plan(a, &pl) != TV_OK) return 0;
+  return pl.ws_bytes;
+}
+
+extern "C" tv_status tree_verify_attn(const tv_attn_args* a, hipStream_t stream) {
+  tv_status st = check_args(a);
+  if (st != TV_OK) return st;
+  if (a->B == 0) return TV_OK;
+  Plan pl;
+  st = make_plan(a, &pl);
+  if (st != TV_OK) return st;
+  if (pl.ws_bytes > 0) {
+    if (!a->workspace || a->workspace_bytes < pl.ws_bytes)
+      return fail(TV_ERR_WORKSPACE, "workspace missing or smaller than required");
+    if (!aligned16(a->workspace)) return fail(TV_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+  }
+  const AttnParams p = make_params(a, pl);
+  const bool bf16 = a->dtype == TV_BF16;
+  hipError_t e = pl.mfma ? launch_attn_mfma(p, a->D, pl.shape, stream)
+                         : launch_attn_valu(p, a->D, bf16, stream);
+  if (e != hipSuccess) return fail(TV_ERR_HIP, hipGetErrorString(e));
+  if (pl.splits > 1) {
+    e = launch_merge(p, a->D, bf16, stream);
+    if (e != hipSuccess) return fail(TV_ERR_HIP, hipGetErrorString(e));
+  }
+  return TV_OK;
+}
+
+extern "C" tv_status tree_meta_from_parent(const int32_t* parent, int32_t parent_sb, int32_t B,
+                                           int32_t N, const int32_t* prefix_len,
+                                           int32_t* depth, uint64_t* bitmask, int32_t* pos,
+                                           hipStream_t stream) {
+  if (B < 0) return fail(TV_ERR_INVALID_ARG, "B < 0");
+  if (N < 1 || N > TV_MAX_NODES) return fail(TV_ERR_INVALID_ARG, "N outside 1..64");
+  if (parent_sb < 0 || (parent_sb > 0 && parent_sb < N))
+    return fail(TV_ERR_INVALID_ARG, "parent_sb must be 0 or >= N");
+  if (B == 0) return TV_OK;
+  if (!parent) return fail(TV_ERR_INVALID_ARG, "parent is null");
+  const hipError_t e =
+      launch_meta_from_parent(parent, parent_sb, B, N, prefix_len, depth, bitmask, pos, stream);
+  if (e != hipSuccess) return fail(TV_ERR_HIP, hipGetErrorString(e));
+  return TV_OK;
+}
+
+extern "C" const char* tv_status_string(tv_status s) {
+  switch (s) {
+    case TV_OK: return "TV_OK";
+    case TV_ERR_INVALID_ARG: return "TV_ERR_INVALID_ARG";
+    case TV_ERR_INVALID_PATH: return "TV_ERR_INVALID_PATH";
+    case TV_ERR_MISSING_PARENT: return "TV_ERR_MISSING_PARENT";
+    case TV_ERR_CAPACITY: return "TV_ERR_CAPACITY";
+    case TV_ERR_UNSUPPORTED: return "TV_ERR_UNSUPPORTED";
+    case TV_ERR_WORKSPACE: return "TV_ERR_WORKSPACE";
+    case TV_ERR_HIP: return "TV_ERR_HIP";
+  }
+  return "TV_ERR_UNKNOWN";
+}
+
+extern "C" const char* tv_last_error(void) { return g_last_error; }
+
+extern "C" int32_t tv_abi_version(void) { return TV_ABI_VERSION; }
+
+extern "C" size_t tv_attn_args_sizeof(void) { return sizeof(tv_attn_args); }

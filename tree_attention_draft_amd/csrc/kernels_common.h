@@ -1,0 +1,109 @@
+// Device helpers shared by the tree-verify kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tv_internal.h"
+
+namespace tv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Ancestor-or-self bitmask of node i from the parent array ("Tree attention mask for
+// draft-tree verification": the kernel expands the parent array instead of reading a
+// dense mask).  Walks at most i + 1 steps because a valid parent index is strictly
+// smaller than its child; a node that breaks the convention keeps only its own bit
+// (and its ancestors found so far), and `ok` turns false.  Never reads outside
+// parent[0 .. N).
+__device__ inline uint64_t ancestor_bits(const int32_t* __restrict__ par, int i, int N,
+                                         bool& ok, int& depth) {
+  uint64_t m = 0;
+  ok = true;
+  depth = 0;
+  int j = i;
+  for (int step = 0; step <= i; ++step) {
+    m |= 1ull << j;
+    const int p = par[j];
+    if (j == 0) {
+      ok = (p == -1);
+      return m;
+    }
+    if (p < 0 || p >= j) {
+      ok = false;
+      return m;
+    }
+    j = p;
+    ++depth;
+  }
+  ok = false;  // unreachable for valid input
+  (void)N;
+  return m;
+}
+
+// Element offset of logical token t of request b, kv head h, in the K or V store.
+__device__ inline int64_t kv_offset(const AttnParams& p, int b, int t, int h) {
+  if (p.paged) {
+    int page_idx, slot;
+    if (p.page_shift >= 0) {
+      page_idx = t >> p.page_shift;
+      slot = t & (p.page_size - 1);
+    } else {
+      page_idx = t / p.page_size;
+      slot = t - page_idx * p.page_size;
+    }
+    const int page = p.page_table[(int64_t)b * p.pages_per_seq + page_idx];
+    return (int64_t)page * p.kv_sb + (int64_t)slot * p.kv_st + (int64_t)h * p.kv_sh;
+  }
+  return (int64_t)b * p.kv_sb + (int64_t)t * p.kv_st + (int64_t)h * p.kv_sh;
+}
+
+// Prefix length of request b, clamped to [0, max_prefix_len] so that a device value that
+// breaks the documented bound can never move a read past max_prefix_len + N.
+__device__ inline int clamped_prefix(const AttnParams& p, int b) {
+  return min(max(p.prefix_len[b], 0), p.max_prefix_len);
+}
+
+// Allowed-key bits of one 64-key tile that starts at logical key kt0, for a row whose
+// node has ancestor-or-self bitmask `anc` (bit i <-> tree key L + i).  Bit j is set iff key
+// kt0 + j is a prefix key (< L) or the tree key of an ancestor-or-self.  Keys at or past
+// L + N never get a bit because `anc` has none at or above N.  kt0 and L are uniform
+// across the workgroup, so the branches are scalar.
+__device__ inline uint64_t tile_allowed(uint64_t anc, int kt0, int L) {
+  const int P = L - kt0;  // prefix keys at the start of the tile (may be <= 0 or >= 64)
+  const uint64_t prefix = P >= 64 ? ~0ull : (P <= 0 ? 0ull : ((1ull << P) - 1ull));
+  uint64_t tree;
+  if (P >= 0)
+    tree = P < 64 ? (anc << P) : 0ull;
+  else
+    tree = -P < 64 ? (anc >> -P) : 0ull;
+  return prefix | tree;
+}
+
+__device__ inline float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ inline float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ inline float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float -> bfloat16 bits, round to nearest even (inputs here are finite or inf).
+__device__ inline uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+}  // namespace tv

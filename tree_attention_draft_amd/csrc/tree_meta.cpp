@@ -1,0 +1,137 @@
+// Host tree-metadata builder: drafter-rank paths -> parent, depth, ancestor bitmask, pos.
+//
+// Method ("Tree attention mask for draft-tree verification", section "A strong answer"):
+// candidates are tuples of drafter ranks under an implicit root (node 0, the last accepted
+// token); distinct candidates become nodes 1.. in (length, lexicographic) order; a node's
+// parent is the node of its one-shorter prefix and a candidate without one is rejected;
+// depth is the tuple length; position id is prefix length + depth; node i may see node j
+// iff j is i or an ancestor.  Because parents precede children in this order, the
+// ancestor bitmask of node i is its parent's bitmask plus bit i -- one pass, O(N).
+//
+// Implementation: sort candidate indices with a comparator over the CSR rank arrays
+// (no copies of the paths), drop adjacent duplicates, and resolve each parent by binary
+// search for the one-shorter prefix among the already-placed nodes of the previous
+// length (they are contiguous and sorted in the node order).
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "tree_verify.h"
+#include "tv_internal.h"
+
+namespace {
+
+struct PathRef {
+  const int32_t* r;
+  int32_t len;
+  int32_t input_index;
+};
+
+// (length, lexicographic) order of the node numbering.
+inline bool path_less(const PathRef& a, const PathRef& b) {
+  if (a.len != b.len) return a.len < b.len;
+  for (int32_t t = 0; t < a.len; ++t)
+    if (a.r[t] != b.r[t]) return a.r[t] < b.r[t];
+  return false;
+}
+
+inline bool same_path(const PathRef& a, const PathRef& b) {
+  return a.len == b.len && std::memcmp(a.r, b.r, sizeof(int32_t) * a.len) == 0;
+}
+
+// Compare the first `len` ranks of `full` with the whole of `node` (node.len == len).
+inline int prefix_cmp(const PathRef& node, const int32_t* full, int32_t len) {
+  for (int32_t t = 0; t < len; ++t) {
+    if (node.r[t] != full[t]) return node.r[t] < full[t] ? -1 : 1;
+  }
+  return 0;
+}
+
+}  // namespace
+
+extern "C" tv_status tree_meta_build(const int32_t* ranks, const int64_t* path_off,
+                                     int32_t num_paths, int32_t prefix_len, int32_t max_nodes,
+                                     int32_t* parent, int32_t* depth, uint64_t* bitmask,
+                                     int32_t* pos, int32_t* num_nodes, int32_t* bad_path) {
+  if (bad_path) *bad_path = -1;
+  if (num_paths < 0) return tv::fail(TV_ERR_INVALID_ARG, "num_paths < 0");
+  if (!path_off || !parent || !depth || !bitmask || !pos || !num_nodes)
+    return tv::fail(TV_ERR_INVALID_ARG, "null output or path_off pointer");
+  if (num_paths > 0 && !ranks && path_off[num_paths] > 0)
+    return tv::fail(TV_ERR_INVALID_ARG, "ranks is null");
+  if (prefix_len < 0) return tv::fail(TV_ERR_INVALID_ARG, "prefix_len < 0");
+  if (max_nodes < 1) return tv::fail(TV_ERR_INVALID_ARG, "max_nodes < 1");
+  if (path_off[0] != 0) return tv::fail(TV_ERR_INVALID_ARG, "path_off[0] != 0");
+
+  std::vector<PathRef> refs;
+  refs.reserve(num_paths);
+  for (int32_t p = 0; p < num_paths; ++p) {
+    const int64_t a = path_off[p], b = path_off[p + 1];
+    if (b < a) return tv::fail(TV_ERR_INVALID_ARG, "path_off is not non-decreasing");
+    if (b - a > INT32_MAX) return tv::fail(TV_ERR_INVALID_ARG, "path too long");
+    if (b == a) {
+      if (bad_path) *bad_path = p;
+      return tv::fail(TV_ERR_INVALID_PATH, "empty path (the root is implicit)");
+    }
+    for (int64_t t = a; t < b; ++t) {
+      if (ranks[t] < 0) {
+        if (bad_path) *bad_path = p;
+        return tv::fail(TV_ERR_INVALID_PATH, "negative rank");
+      }
+    }
+    refs.push_back(PathRef{ranks + a, static_cast<int32_t>(b - a), p});
+  }
+  // stable sort keeps the first input occurrence first among duplicates
+  std::stable_sort(refs.begin(), refs.end(), path_less);
+  std::vector<PathRef> nodes;
+  nodes.reserve(refs.size() + 1);
+  nodes.push_back(PathRef{nullptr, 0, -1});  // root
+  for (const PathRef& r : refs)
+    if (nodes.size() == 1 || !same_path(nodes.back(), r)) nodes.push_back(r);
+
+  const int64_t n = static_cast<int64_t>(nodes.size());
+  if (n > max_nodes || n > TV_MAX_NODES) {
+    return tv::fail(TV_ERR_CAPACITY, "tree has more nodes than the output capacity");
+  }
+
+  // Nodes are grouped by length; group g covers [begin, end) of one length.
+  struct Group { int32_t len; int64_t begin, end; };
+  std::vector<Group> groups;
+  for (int64_t i = 1; i < n; ++i) {
+    if (groups.empty() || groups.back().len != nodes[i].len)
+      groups.push_back(Group{nodes[i].len, i, i + 1});
+    else
+      groups.back().end = i + 1;
+  }
+  parent[0] = -1;
+  depth[0] = 0;
+  bitmask[0] = 1ull;
+  size_t g = 0;
+  for (int64_t i = 1; i < n; ++i) {
+    const PathRef& me = nodes[i];
+    while (groups[g].end <= i) ++g;  // groups[g] holds node i
+    int64_t found = -1;
+    if (me.len == 1) {
+      found = 0;
+    } else if (g > 0 && groups[g - 1].len == me.len - 1) {
+      int64_t lo = groups[g - 1].begin, hi = groups[g - 1].end;  // binary search [lo, hi)
+      while (lo < hi) {
+        const int64_t mid = lo + (hi - lo) / 2;
+        const int c = prefix_cmp(nodes[mid], me.r, me.len - 1);
+        if (c == 0) { found = mid; break; }
+        if (c < 0) lo = mid + 1; else hi = mid;
+      }
+    }
+    if (found < 0) {
+      if (bad_path) *bad_path = me.input_index;
+      return tv::fail(TV_ERR_MISSING_PARENT, "a path's one-shorter prefix is not a node");
+    }
+    parent[i] = static_cast<int32_t>(found);
+    depth[i] = me.len;
+    bitmask[i] = bitmask[found] | (1ull << i);
+  }
+  for (int64_t i = 0; i < n; ++i) pos[i] = prefix_len + depth[i];
+  *num_nodes = static_cast<int32_t>(n);
+  return TV_OK;
+}

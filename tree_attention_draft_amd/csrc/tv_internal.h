@@ -1,0 +1,57 @@
+// Internal declarations shared by the host glue and the kernel launchers of libtreeverify.
+#pragma once
+#include <cstdint>
+
+#include <hip/hip_runtime_api.h>
+
+#include "tree_verify.h"
+
+namespace tv {
+
+// Records a detail string for tv_last_error() on this thread and returns `s`.
+tv_status fail(tv_status s, const char* detail);
+
+constexpr int kKeysPerTile = 64;  // keys staged in LDS per step of the streaming loop
+
+// Everything a kernel needs, passed by value.  Strides in elements.
+struct AttnParams {
+  const void* q;
+  int64_t q_sb, q_sn, q_sh;
+  const void* k;
+  const void* v;
+  int64_t kv_sb, kv_st, kv_sh;
+  const int32_t* page_table;
+  int32_t page_size, pages_per_seq, paged;
+  int32_t page_shift;  // log2(page_size) when it is a power of two, else -1
+  const int32_t* parent;
+  int32_t parent_sb;
+  const int32_t* prefix_len;
+  int32_t max_prefix_len;  // host bound; device values are clamped to [0, this]
+  void* out;
+  int64_t o_sb, o_sn, o_sh;
+  float* lse;
+  float* ws_o;    // [B][Hkv][S][R][D] normalised partial outputs (split > 1)
+  float* ws_lse;  // [B][Hkv][S][R]    log2-domain partial LSE
+  int32_t B, N, Hq, Hkv, g, R;
+  int32_t num_splits;  // S
+  int32_t chunk;       // keys per split, a multiple of kKeysPerTile
+  int32_t row_chunks;  // workgroups along the packed-row dimension
+  int32_t rows_per_wg; // packed rows one workgroup covers
+  float scale_log2;    // sm_scale * log2(e)
+};
+
+// MFMA kernel shape: each wave owns `tpw` 16-row tiles; `nw` waves per workgroup.
+struct MfmaShape {
+  int tpw, nw;
+};
+
+hipError_t launch_attn_mfma(const AttnParams& p, int D, MfmaShape shape, hipStream_t s);
+hipError_t launch_attn_valu(const AttnParams& p, int D, bool bf16, hipStream_t s);
+hipError_t launch_merge(const AttnParams& p, int D, bool bf16, hipStream_t s);
+hipError_t launch_meta_from_parent(const int32_t* parent, int32_t parent_sb, int32_t B,
+                                   int32_t N, const int32_t* prefix_len, int32_t* depth,
+                                   uint64_t* bitmask, int32_t* pos, hipStream_t s);
+
+constexpr int kValuRowsPerWg = 16;  // 4 waves x 4 rows
+
+}  // namespace tv

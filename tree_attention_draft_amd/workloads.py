@@ -17,6 +17,9 @@ Recipe (stated once here, used by tests and the benchmark):
 * Paged KV: page size 16, pool = B * ceil((L + N) / 16) pages, physical ids one random
   permutation of the pool.
 """
+import concurrent.futures
+import os
+
 import numpy as np
 
 BF16_NAN_BITS = 0x7FC0
@@ -60,14 +63,23 @@ def normal_f32(rng, shape):
     return rng.standard_normal(size=shape, dtype=np.float32)
 
 
-def f32_to_bf16_bits(x):
-    """Round float32 values to bfloat16 (nearest, ties to even); returns uint16 bits."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    bits = rounded.astype(np.uint16)
-    nan = np.isnan(x)
-    if nan.any():
-        bits[nan] = BF16_NAN_BITS
+def f32_to_bf16_bits(x, finite=False):
+    """Round float32 values to bfloat16 (nearest, ties to even); returns uint16 bits.
+    Finite inputs only need 32-bit arithmetic (the largest finite pattern plus the rounding
+    increment stays below 2**32); NaN maps to the canonical bfloat16 NaN.  ``finite=True``
+    skips the NaN scan for data known to be finite."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    r = u >> np.uint32(16)
+    r &= np.uint32(1)
+    r += u
+    r += np.uint32(0x7FFF)
+    r >>= np.uint32(16)
+    bits = r.astype(np.uint16)
+    if not finite:
+        nan = np.isnan(x)
+        if nan.any():
+            bits[nan] = BF16_NAN_BITS
     return bits
 
 
@@ -142,3 +154,76 @@ def prefix_lengths(spec, batch=None):
         rng = np.random.Generator(np.random.PCG64(4000 + spec["k"]))
         return ragged_lengths(rng, B, L[0], L[1])
     return np.full(B, L, dtype=np.int32)
+
+
+def request_tensors(seed, b, n_nodes, prefix_len, hq, hkv, d, k_scale=False):
+    """float32 Q [N, Hq, D] and logical K, V [L + N, Hkv, D] of request ``b``.
+
+    Every request draws from its own PCG64 stream (seeded with ``(seed, b)``), so any
+    request can be regenerated alone.  ``k_scale`` multiplies K by 1/sqrt(D).
+    """
+    rng = np.random.Generator(np.random.PCG64([seed, b]))
+    q = normal_f32(rng, (n_nodes, hq, d))
+    k = normal_f32(rng, (prefix_len + n_nodes, hkv, d))
+    v = normal_f32(rng, (prefix_len + n_nodes, hkv, d))
+    if k_scale:
+        k *= np.float32(1.0 / np.sqrt(d))
+    return q, k, v
+
+
+def encode(x, dtype):
+    """Storage form of finite float32 values: bf16 bits (uint16) or float32 itself."""
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x, finite=True)
+    return np.ascontiguousarray(x, np.float32)
+
+
+def nan_fill(shape, dtype):
+    if dtype == "bf16":
+        return np.full(shape, BF16_NAN_BITS, dtype=np.uint16)
+    return np.full(shape, np.nan, dtype=np.float32)
+
+
+def build_batch(seed, prefix_lens, n_nodes, hq, hkv, d, dtype, k_scale=False, page_size=0,
+                page_seed=None):
+    """Host arrays for one batch.
+
+    Returns a dict with ``q`` [B, N, Hq, D] and either contiguous ``k``, ``v``
+    [B, max L + N, Hkv, D] (NaN beyond each request's L + N) or, when ``page_size`` > 0,
+    pools ``k``, ``v`` [pages, page_size, Hkv, D] plus ``page_table`` [B, pages_per_seq]
+    (slots past a request's L + N are NaN).  Values are uint16 bf16 bits or float32.
+    """
+    B = len(prefix_lens)
+    Lmax = int(max(prefix_lens)) if B else 0
+    S = Lmax + n_nodes
+    q = np.empty((B, n_nodes, hq, d), np.uint16 if dtype == "bf16" else np.float32)
+    out = {"q": q, "prefix_len": np.asarray(prefix_lens, np.int32)}
+    if page_size:
+        prng = np.random.Generator(np.random.PCG64(page_seed))
+        table, n_pages = page_table(prng, B, S, page_size)
+        kpool = nan_fill((n_pages, page_size, hkv, d), dtype)
+        vpool = nan_fill((n_pages, page_size, hkv, d), dtype)
+        out.update(k=kpool, v=vpool, page_table=table, page_size=page_size)
+    else:
+        kc = nan_fill((B, S, hkv, d), dtype)
+        vc = nan_fill((B, S, hkv, d), dtype)
+        out.update(k=kc, v=vc)
+    def fill(b):
+        L = int(prefix_lens[b])
+        qb, kb, vb = request_tensors(seed, b, n_nodes, L, hq, hkv, d, k_scale)
+        q[b] = encode(qb, dtype)
+        kb, vb = encode(kb, dtype), encode(vb, dtype)
+        if page_size:
+            T = L + n_nodes
+            for pi in range(-(-T // page_size)):
+                lo, hi = pi * page_size, min(T, (pi + 1) * page_size)
+                out["k"][table[b, pi], :hi - lo] = kb[lo:hi]
+                out["v"][table[b, pi], :hi - lo] = vb[lo:hi]
+        else:
+            out["k"][b, :L + n_nodes] = kb
+            out["v"][b, :L + n_nodes] = vb
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(fill, range(B)))
+    return out
