@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of the tree-verification attention pass on one MI355X.
+
+One step is the whole hot path for one batch: the host C++ builder turns every request's
+candidate rank paths into parent/depth/bitmask/position arrays, the parent arrays are
+copied to the device, the device metadata kernel expands them, and the attention kernel
+(plus the merge kernel when keys are split) verifies every node of every tree.  The host
+builder of step k+1 overlaps the device work of step k (double-buffered pinned arrays).
+
+Default workload: B=64 requests, prefix L=4096, N=33-node random draft trees (depth <= 8),
+GQA 32 query / 8 kv heads, D=128, bf16, contiguous KV -- 1.117 GB of algorithmic traffic
+per step.  Inputs are seeded synthetic Gaussians and sit in HBM before timing starts; the
+working set exceeds the 256 MB last-level cache, so no flush is needed between steps.
+
+Prints ONE JSON line.  ``value`` = verified tree nodes per second over the timed steps.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tree-verify attn: verified nodes/s + HBM GB/s % peak at B=64,L=4k,N=33"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+COUNTERS = os.path.join(ROOT, "profiles", "tv_attn_mfma_b64_l4096_n33.counters.json")
+KERNEL_SOURCES = ["attn_mfma.hip", "kernels_common.h", "tv_internal.h"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "tree_attention_draft_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(prefix_lens, N, Hq, Hkv, D, elem, paged_page=0):
+    """Bytes one attention launch must move at minimum: K and V over [0, L+N), Q read,
+    out written, LSE written, parent array and prefix length read (and the page table)."""
+    total = 0
+    for L in prefix_lens:
+        T = int(L) + N
+        total += T * Hkv * D * elem * 2 + 2 * N * Hq * D * elem + 4 * N * Hq + 4 * N + 4
+        if paged_page:
+            total += 4 * math.ceil(T / paged_page)
+    return total
+
+
+def algorithmic_flops(prefix_lens, depths, Hq, D):
+    """QK^T and PV flops over the keys each node may see (prefix + depth + 1)."""
+    total = 0
+    for L, dep in zip(prefix_lens, depths):
+        total += sum(4 * D * Hq * (int(L) + int(d) + 1) for d in dep)
+    return total
+
+
+def cpu_baseline(host, trees_parent, prefix_lens, N, budget_s):
+    """Time the fp64 oracle (as it stands) on whole requests until the budget is spent."""
+    import numpy as np
+    from oracle import attn as oattn
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = 1
+    done = 0
+    t0 = time.perf_counter()
+    while done < len(prefix_lens) and time.perf_counter() - t0 < budget_s:
+        b = done
+        T = int(prefix_lens[b]) + N
+        q = oattn.bf16_bits_to_f64(host["q"][b])
+        k = oattn.bf16_bits_to_f64(host["k"][b, :T])
+        v = oattn.bf16_bits_to_f64(host["v"][b, :T])
+        oattn.tree_attention_request(q, k, v, trees_parent[b], int(prefix_lens[b]))
+        done += 1
+    el = time.perf_counter() - t0
+    return {"value": done * N / el, "unit": "nodes/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {len(prefix_lens)} requests (all nodes and heads), fp64 "
+                      f"numpy oracle, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 1 GiB device copy (counter scaling reference)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world}); multi-GPU sharding is design-only.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import tree_attention_draft_amd as tv
+    from oracle import attn as oattn
+    from oracle import meta as ometa
+    from tree_attention_draft_amd import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    spec = workloads.WORKLOADS["b64_l4096_n33"]
+    B, N, Hq, Hkv, D = spec["B"], spec["N"], spec["Hq"], spec["Hkv"], spec["D"]
+    trees, _ = workloads.trees_for(spec)
+    L = workloads.prefix_lengths(spec)
+    Lmax = int(L.max())
+    print(f"[bench] generating inputs B={B} L={Lmax} N={N} Hq={Hq} Hkv={Hkv} D={D}",
+          file=sys.stderr, flush=True)
+    host = workloads.build_batch(1000 + spec["k"], L, N, Hq, Hkv, D, "bf16")
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = up(host["q"]), up(host["k"]), up(host["v"])
+    prefix_dev = torch.from_numpy(L).to(dev)
+    packed = tv.PackedTrees(trees)
+    pin = [torch.empty((B, N), dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    pin_np = [p.numpy() for p in pin]
+    h_depth = np.empty((B, N), np.int32)
+    h_mask = np.empty((B, N), np.uint64)
+    h_pos = np.empty((B, N), np.int32)
+    parent_dev = [torch.empty((B, N), dtype=torch.int32, device=dev) for _ in range(2)]
+    d_depth = torch.empty((B, N), dtype=torch.int32, device=dev)
+    d_mask = torch.empty((B, N), dtype=torch.int64, device=dev)
+    d_pos = torch.empty((B, N), dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, N, Hq), dtype=torch.float32, device=dev)
+    ws_bytes = tv.tree_verify_attn_workspace_size(q, k, v, parent_dev[0], prefix_dev, Lmax)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    copy_done = [torch.cuda.Event() for _ in range(2)]
+    for e in copy_done:
+        e.record()
+    total = args.warmup + args.steps
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(total)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(total)]
+
+    def step(i):
+        s = i % 2
+        copy_done[s].synchronize()        # the copy that last read this pinned slot is done
+        tv.tree_meta_build_batch(packed, L, N, parent=pin_np[s], depth=h_depth,
+                                 bitmask=h_mask, pos=h_pos)
+        parent_dev[s].copy_(pin[s], non_blocking=True)
+        copy_done[s].record()
+        tv.tree_meta_from_parent(parent_dev[s], prefix_dev, depth=d_depth, bitmask=d_mask,
+                                 pos=d_pos)
+        ev_a[i].record()
+        tv.tree_verify_attn(q, k, v, parent_dev[s], prefix_dev, Lmax, out=out, lse=lse,
+                            workspace=ws)
+        ev_b[i].record()
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print("[bench] timed steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for i in range(args.warmup, total):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    kern_ms = [ev_a[i].elapsed_time(ev_b[i]) for i in range(args.warmup, total)]
+    kern_avg_s = float(np.mean(kern_ms)) / 1e3
+
+    # metadata and a sampled parity check against the oracle (outside the timed region)
+    ref_parent = [ometa.build_from_paths(t, 0)["parent"] for t in trees]
+    assert all(pin_np[0][b].tolist() == ref_parent[b] for b in range(B))
+    out_h = out.float().cpu().numpy()
+    lse_h = lse.cpu().numpy()
+    worst = 0.0
+    sample = [0, B - 1]
+    for b in sample:
+        T = int(L[b]) + N
+        o, l = oattn.tree_attention_request(
+            oattn.bf16_bits_to_f64(host["q"][b]), oattn.bf16_bits_to_f64(host["k"][b, :T]),
+            oattn.bf16_bits_to_f64(host["v"][b, :T]), ref_parent[b], int(L[b]))
+        worst = max(worst, float(np.abs(out_h[b] - o).max()), float(np.abs(lse_h[b] - l).max()))
+    parity_ok = worst <= 2e-2
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    alg_bytes = algorithmic_bytes(L, N, Hq, Hkv, D, 2)
+    depths = [ometa.meta_from_parent(p, 0)["depth"] for p in ref_parent]
+    flops = algorithmic_flops(L, depths, Hq, D)
+    achieved = alg_bytes / kern_avg_s / 1e9
+    traffic = None
+    if os.path.exists(COUNTERS):
+        with open(COUNTERS) as fh:
+            c = json.load(fh)
+        if c.get("kernel_source_hash") == kernel_source_hash():
+            traffic = c.get("hbm_bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": B * N * args.steps / elapsed,
+        "unit": "nodes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "tree-verify attention: B=64 requests, prefix L=4096, N=33-node "
+                        "random draft trees (depth<=8), GQA 32q/8kv, D=128, bf16, "
+                        "contiguous KV",
+            "B": B, "L": Lmax, "N": N, "Hq": Hq, "Hkv": Hkv, "D": D,
+            "kv_layout": "contiguous", "splits": "auto",
+            "workspace_bytes": ws_bytes,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "kernel": "tv_attn_mfma_kernel",
+            "kernel_avg_us": kern_avg_s * 1e6,
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "mfma_tflops": flops / kern_avg_s / 1e12,
+            "mfma_frac": flops / kern_avg_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        },
+        "parity": {"requests": sample, "max_abs_err": worst, "tol": 2e-2, "ok": parity_ok},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(host, ref_parent, L, N, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    if not parity_ok:
+        sys.exit(1)
+
+
+if __name__ == "__main__":
+    main()

@@ -79,6 +79,28 @@ tv_status tree_meta_build(const int32_t* ranks, const int64_t* path_off, int32_t
                           int32_t* num_nodes, int32_t* bad_path);
 
 /*
+ * tree_meta_build_batch -- tree_meta_build for B requests in one call, writing dense
+ * [B, N] outputs ready for tree_verify_attn.
+ *
+ * Input (host): tree b owns candidates tree_off[b] .. tree_off[b+1]-1 of the CSR path list
+ * (ranks/path_off as for tree_meta_build; tree_off has B + 1 entries, tree_off[0] = 0);
+ * prefix_len[b] is its cached prefix length; N is the node count every output row holds.
+ * Output (host, caller-owned): parent, depth, pos [B, N] int32 and bitmask [B, N] uint64;
+ * num_nodes[b] = the tree's own node count.  A tree with fewer than N nodes is padded with
+ * extra leaves under the root (parent 0) so that the row still satisfies the parent
+ * convention; callers ignore outputs of nodes at or past num_nodes[b].
+ * Errors: as tree_meta_build for the first failing tree; *bad_tree names it (may be NULL)
+ * and *bad_path the offending path's index within that tree.  TV_ERR_CAPACITY when a tree
+ * has more than N nodes.
+ */
+tv_status tree_meta_build_batch(const int32_t* ranks, const int64_t* path_off,
+                                const int64_t* tree_off, int32_t B,
+                                const int32_t* prefix_len, int32_t N,
+                                int32_t* parent, int32_t* depth, uint64_t* bitmask,
+                                int32_t* pos, int32_t* num_nodes, int32_t* bad_tree,
+                                int32_t* bad_path);
+
+/*
  * tree_meta_from_parent -- the same metadata from device-resident parent arrays (the
  * parent-array form a kernel "expands per tile": "Tree attention mask for draft-tree
  * verification", paragraph after the build listing).
@@ -146,9 +168,10 @@ typedef struct tv_attn_args {
 
 /*
  * tree_verify_attn_workspace_size -- bytes of device workspace the call needs for these
- * arguments (0 when one split covers every request).  Host only; the automatic split
- * count depends on the current device's compute-unit count.  Returns 0 for arguments
- * tree_verify_attn would reject.
+ * arguments (0 when one split covers every request).  Host only; depends on shapes,
+ * strides, max_prefix_len, num_splits and path only (pointer fields are not read), and the
+ * automatic split count on the current device's compute-unit count.  Returns 0 for
+ * shapes tree_verify_attn would reject.
  */
 size_t tree_verify_attn_workspace_size(const tv_attn_args* a);
 

@@ -186,8 +186,16 @@ def test_attn_argument_checks(kw, status):
     a = base_args(**kw)
     L = tv.lib()
     assert L.tree_verify_attn(ctypes.byref(a), None) == status
-    assert L.tree_verify_attn_workspace_size(ctypes.byref(a)) == 0
     assert L.tv_last_error().decode() != ""
+    pointer_only = any(k in ("q", "k", "parent", "prefix_len", "out") for k in kw)
+    if not pointer_only:
+        assert L.tree_verify_attn_workspace_size(ctypes.byref(a)) == 0
+
+
+def test_workspace_size_ignores_pointers():
+    a = base_args(B=1, max_prefix_len=32768, num_splits=8, q=None, k=None, v=None,
+                  out=None, parent=None, prefix_len=None)
+    assert tv.lib().tree_verify_attn_workspace_size(ctypes.byref(a)) == 8 * 8 * 40 * 129 * 4
 
 
 def test_attn_empty_batch_is_noop():

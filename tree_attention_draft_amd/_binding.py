@@ -23,7 +23,7 @@ PATHS = {"auto": 0, "valu": 1, "mfma": 2}
 MAX_NODES = 64
 
 # Every symbol include/tree_verify.h declares.
-EXPORTS = ["tree_meta_build", "tree_meta_from_parent", "tree_verify_attn_workspace_size",
+EXPORTS = ["tree_meta_build", "tree_meta_build_batch", "tree_meta_from_parent", "tree_verify_attn_workspace_size",
            "tree_verify_attn", "tv_status_string", "tv_last_error", "tv_abi_version",
            "tv_attn_args_sizeof"]
 
@@ -75,6 +75,8 @@ def lib():
     i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
     L.tree_meta_build.restype = i32
     L.tree_meta_build.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+    L.tree_meta_build_batch.restype = i32
+    L.tree_meta_build_batch.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp]
     L.tree_meta_from_parent.restype = i32
     L.tree_meta_from_parent.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp]
     L.tree_verify_attn_workspace_size.restype = ctypes.c_size_t
@@ -122,6 +124,47 @@ def tree_meta_build(paths, prefix_len, max_nodes=MAX_NODES):
     k = n.value
     return {"parent": parent[:k].copy(), "depth": depth[:k].copy(),
             "bitmask": bitmask[:k].copy(), "pos": pos[:k].copy()}
+
+
+class PackedTrees:
+    """Candidate paths of B requests packed once as CSR arrays (host memory), ready for
+    repeated tree_meta_build_batch calls."""
+
+    def __init__(self, trees):
+        offs, flat, toff = [0], [], [0]
+        for paths in trees:
+            for p in paths:
+                flat.extend(int(x) for x in p)
+                offs.append(len(flat))
+            toff.append(len(offs) - 1)
+        self.ranks = np.asarray(flat if flat else [0], dtype=np.int32)
+        self.path_off = np.asarray(offs, dtype=np.int64)
+        self.tree_off = np.asarray(toff, dtype=np.int64)
+        self.B = len(trees)
+
+
+def tree_meta_build_batch(packed, prefix_len, N, parent=None, depth=None, bitmask=None,
+                          pos=None):
+    """Build all B trees of ``packed`` (a :class:`PackedTrees`) into dense [B, N] host
+    arrays.  Output arrays may be passed in (e.g. pinned buffers viewed as numpy)."""
+    B = packed.B
+    pl = np.ascontiguousarray(prefix_len, dtype=np.int32)
+    parent = np.empty((B, N), np.int32) if parent is None else parent
+    depth = np.empty((B, N), np.int32) if depth is None else depth
+    bitmask = np.empty((B, N), np.uint64) if bitmask is None else bitmask
+    pos = np.empty((B, N), np.int32) if pos is None else pos
+    nn = np.empty(B, np.int32)
+    bt, bp = ctypes.c_int32(-1), ctypes.c_int32(-1)
+    st = lib().tree_meta_build_batch(
+        packed.ranks.ctypes.data, packed.path_off.ctypes.data, packed.tree_off.ctypes.data,
+        B, pl.ctypes.data, int(N), parent.ctypes.data, depth.ctypes.data,
+        bitmask.ctypes.data, pos.ctypes.data, nn.ctypes.data, ctypes.byref(bt),
+        ctypes.byref(bp))
+    if st != TV_OK:
+        raise TreeVerifyError(st, lib().tv_last_error().decode() + f" (tree {bt.value})",
+                              bp.value)
+    return {"parent": parent, "depth": depth, "bitmask": bitmask, "pos": pos,
+            "num_nodes": nn}
 
 
 # ------------------------------------------------------------------- device side -----

@@ -61,7 +61,7 @@ MfmaShape pick_mfma_shape(int qt, int* row_chunks) {
   return MfmaShape{4, 8};
 }
 
-tv_status check_args(const tv_attn_args* a) {
+tv_status check_args(const tv_attn_args* a, bool pointers) {
   if (!a) return fail(TV_ERR_INVALID_ARG, "args is null");
   if (a->dtype != TV_BF16 && a->dtype != TV_F32) return fail(TV_ERR_INVALID_ARG, "bad dtype");
   if (a->B < 0) return fail(TV_ERR_INVALID_ARG, "B < 0");
@@ -81,7 +81,7 @@ tv_status check_args(const tv_attn_args* a) {
   if (!(a->sm_scale >= 0.f) || !std::isfinite(a->sm_scale))
     return fail(TV_ERR_INVALID_ARG, "sm_scale must be finite and >= 0");
   if (a->B == 0) return TV_OK;
-  if (!a->q || !a->k || !a->v || !a->parent || !a->prefix_len || !a->out)
+  if (pointers && (!a->q || !a->k || !a->v || !a->parent || !a->prefix_len || !a->out))
     return fail(TV_ERR_INVALID_ARG, "null q, k, v, parent, prefix_len or out");
   if (a->parent_sb < 0) return fail(TV_ERR_INVALID_ARG, "parent_sb < 0");
   if (a->parent_sb > 0 && a->parent_sb < a->N)
@@ -93,10 +93,11 @@ tv_status check_args(const tv_attn_args* a) {
     if (s < 0 || s % vec != 0)
       return fail(TV_ERR_INVALID_ARG, "strides must be >= 0 and multiples of 16 bytes");
   }
-  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->out))
+  if (pointers &&
+      (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->out)))
     return fail(TV_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
   if (a->kv_layout == TV_KV_PAGED) {
-    if (!a->page_table || a->page_size < 1 || a->pages_per_seq < 1)
+    if ((pointers && !a->page_table) || a->page_size < 1 || a->pages_per_seq < 1)
       return fail(TV_ERR_INVALID_ARG, "paged KV needs page_table, page_size, pages_per_seq");
     const int64_t need = ((int64_t)a->max_prefix_len + a->N + a->page_size - 1) / a->page_size;
     if (a->pages_per_seq < need)
@@ -206,14 +207,14 @@ tv_status fail(tv_status s, const char* detail) {
 using namespace tv;
 
 extern "C" size_t tree_verify_attn_workspace_size(const tv_attn_args* a) {
-  if (check_args(a) != TV_OK || a->B == 0) return 0;
+  if (check_args(a, false) != TV_OK || a->B == 0) return 0;
   Plan pl;
   if (make_plan(a, &pl) != TV_OK) return 0;
   return pl.ws_bytes;
 }
 
 extern "C" tv_status tree_verify_attn(const tv_attn_args* a, hipStream_t stream) {
-  tv_status st = check_args(a);
+  tv_status st = check_args(a, true);
   if (st != TV_OK) return st;
   if (a->B == 0) return TV_OK;
   Plan pl;

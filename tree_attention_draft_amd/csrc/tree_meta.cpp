@@ -8,8 +8,8 @@
 // iff j is i or an ancestor.  Because parents precede children in this order, the
 // ancestor bitmask of node i is its parent's bitmask plus bit i -- one pass, O(N).
 //
-// Implementation: sort candidate indices with a comparator over the CSR rank arrays
-// (no copies of the paths), drop adjacent duplicates, and resolve each parent by binary
+// Implementation: sort references into the CSR rank arrays (no copies of the paths;
+// thread-local scratch, so a batch allocates nothing per tree), drop adjacent duplicates, and resolve each parent by binary
 // search for the one-shorter prefix among the already-placed nodes of the previous
 // length (they are contiguous and sorted in the node order).
 #include <algorithm>
@@ -50,57 +50,61 @@ inline int prefix_cmp(const PathRef& node, const int32_t* full, int32_t len) {
 
 }  // namespace
 
-extern "C" tv_status tree_meta_build(const int32_t* ranks, const int64_t* path_off,
-                                     int32_t num_paths, int32_t prefix_len, int32_t max_nodes,
-                                     int32_t* parent, int32_t* depth, uint64_t* bitmask,
-                                     int32_t* pos, int32_t* num_nodes, int32_t* bad_path) {
-  if (bad_path) *bad_path = -1;
-  if (num_paths < 0) return tv::fail(TV_ERR_INVALID_ARG, "num_paths < 0");
-  if (!path_off || !parent || !depth || !bitmask || !pos || !num_nodes)
-    return tv::fail(TV_ERR_INVALID_ARG, "null output or path_off pointer");
-  if (num_paths > 0 && !ranks && path_off[num_paths] > 0)
-    return tv::fail(TV_ERR_INVALID_ARG, "ranks is null");
-  if (prefix_len < 0) return tv::fail(TV_ERR_INVALID_ARG, "prefix_len < 0");
-  if (max_nodes < 1) return tv::fail(TV_ERR_INVALID_ARG, "max_nodes < 1");
-  if (path_off[0] != 0) return tv::fail(TV_ERR_INVALID_ARG, "path_off[0] != 0");
+namespace {
 
-  std::vector<PathRef> refs;
-  refs.reserve(num_paths);
-  for (int32_t p = 0; p < num_paths; ++p) {
+struct Scratch {
+  std::vector<PathRef> refs, nodes;
+  struct Group { int32_t len; int64_t begin, end; };
+  std::vector<Group> groups;
+};
+
+// One tree from candidates [p0, p1) of a CSR list with absolute offsets path_off[].
+// Writes up to `cap` nodes; *bad gets the offending candidate's index relative to p0.
+tv_status build_one(const int32_t* ranks, const int64_t* path_off, int64_t p0, int64_t p1,
+                    int32_t prefix_len, int32_t cap, int32_t* parent, int32_t* depth,
+                    uint64_t* bitmask, int32_t* pos, int32_t* num_nodes, int32_t* bad) {
+  thread_local Scratch sc;
+  std::vector<PathRef>& refs = sc.refs;
+  std::vector<PathRef>& nodes = sc.nodes;
+  refs.clear();
+  nodes.clear();
+  sc.groups.clear();
+  for (int64_t p = p0; p < p1; ++p) {
     const int64_t a = path_off[p], b = path_off[p + 1];
+    const int32_t rel = static_cast<int32_t>(p - p0);
     if (b < a) return tv::fail(TV_ERR_INVALID_ARG, "path_off is not non-decreasing");
     if (b - a > INT32_MAX) return tv::fail(TV_ERR_INVALID_ARG, "path too long");
     if (b == a) {
-      if (bad_path) *bad_path = p;
+      *bad = rel;
       return tv::fail(TV_ERR_INVALID_PATH, "empty path (the root is implicit)");
     }
     for (int64_t t = a; t < b; ++t) {
       if (ranks[t] < 0) {
-        if (bad_path) *bad_path = p;
+        *bad = rel;
         return tv::fail(TV_ERR_INVALID_PATH, "negative rank");
       }
     }
-    refs.push_back(PathRef{ranks + a, static_cast<int32_t>(b - a), p});
+    refs.push_back(PathRef{ranks + a, static_cast<int32_t>(b - a), rel});
   }
-  // stable sort keeps the first input occurrence first among duplicates
-  std::stable_sort(refs.begin(), refs.end(), path_less);
-  std::vector<PathRef> nodes;
-  nodes.reserve(refs.size() + 1);
+  // (length, lexicographic) order; among duplicates the first input occurrence first
+  std::sort(refs.begin(), refs.end(), [](const PathRef& x, const PathRef& y) {
+    if (path_less(x, y)) return true;
+    if (path_less(y, x)) return false;
+    return x.input_index < y.input_index;
+  });
   nodes.push_back(PathRef{nullptr, 0, -1});  // root
   for (const PathRef& r : refs)
     if (nodes.size() == 1 || !same_path(nodes.back(), r)) nodes.push_back(r);
 
   const int64_t n = static_cast<int64_t>(nodes.size());
-  if (n > max_nodes || n > TV_MAX_NODES) {
+  if (n > cap || n > TV_MAX_NODES)
     return tv::fail(TV_ERR_CAPACITY, "tree has more nodes than the output capacity");
-  }
 
-  // Nodes are grouped by length; group g covers [begin, end) of one length.
-  struct Group { int32_t len; int64_t begin, end; };
-  std::vector<Group> groups;
+  // nodes are grouped by length; a parent lives in the group one shorter
+  auto& groups = sc.groups;
   for (int64_t i = 1; i < n; ++i) {
     if (groups.empty() || groups.back().len != nodes[i].len)
-      groups.push_back(Group{nodes[i].len, i, i + 1});
+      groups.push_back(Scratch::Group{nodes[i].len, i, i + 1});
     else
       groups.back().end = i + 1;
   }
@@ -124,7 +128,7 @@ extern "C" tv_status tree_meta_build(const int32_t* ranks, const int64_t* path_o
       }
     }
     if (found < 0) {
-      if (bad_path) *bad_path = me.input_index;
+      *bad = me.input_index;
       return tv::fail(TV_ERR_MISSING_PARENT, "a path's one-shorter prefix is not a node");
     }
     parent[i] = static_cast<int32_t>(found);
@@ -133,5 +137,73 @@ extern "C" tv_status tree_meta_build(const int32_t* ranks, const int64_t* path_o
   }
   for (int64_t i = 0; i < n; ++i) pos[i] = prefix_len + depth[i];
   *num_nodes = static_cast<int32_t>(n);
+  return TV_OK;
+}
+
+bool prefix_ok(int32_t L) { return L >= 0 && L <= INT32_MAX - 2 * TV_MAX_NODES; }
+
+}  // namespace
+
+extern "C" tv_status tree_meta_build(const int32_t* ranks, const int64_t* path_off,
+                                     int32_t num_paths, int32_t prefix_len, int32_t max_nodes,
+                                     int32_t* parent, int32_t* depth, uint64_t* bitmask,
+                                     int32_t* pos, int32_t* num_nodes, int32_t* bad_path) {
+  if (bad_path) *bad_path = -1;
+  if (num_paths < 0) return tv::fail(TV_ERR_INVALID_ARG, "num_paths < 0");
+  if (!path_off || !parent || !depth || !bitmask || !pos || !num_nodes)
+    return tv::fail(TV_ERR_INVALID_ARG, "null output or path_off pointer");
+  if (path_off[0] != 0) return tv::fail(TV_ERR_INVALID_ARG, "path_off[0] != 0");
+  if (num_paths > 0 && !ranks && path_off[num_paths] > 0)
+    return tv::fail(TV_ERR_INVALID_ARG, "ranks is null");
+  if (!prefix_ok(prefix_len)) return tv::fail(TV_ERR_INVALID_ARG, "prefix_len out of range");
+  if (max_nodes < 1) return tv::fail(TV_ERR_INVALID_ARG, "max_nodes < 1");
+  int32_t bad = -1;
+  const tv_status st = build_one(ranks, path_off, 0, num_paths, prefix_len, max_nodes, parent,
+                                 depth, bitmask, pos, num_nodes, &bad);
+  if (bad_path) *bad_path = bad;
+  return st;
+}
+
+extern "C" tv_status tree_meta_build_batch(const int32_t* ranks, const int64_t* path_off,
+                                           const int64_t* tree_off, int32_t B,
+                                           const int32_t* prefix_len, int32_t N,
+                                           int32_t* parent, int32_t* depth, uint64_t* bitmask,
+                                           int32_t* pos, int32_t* num_nodes, int32_t* bad_tree,
+                                           int32_t* bad_path) {
+  if (bad_tree) *bad_tree = -1;
+  if (bad_path) *bad_path = -1;
+  if (B < 0) return tv::fail(TV_ERR_INVALID_ARG, "B < 0");
+  if (N < 1 || N > TV_MAX_NODES) return tv::fail(TV_ERR_INVALID_ARG, "N outside 1..64");
+  if (B == 0) return TV_OK;
+  if (!path_off || !tree_off || !prefix_len || !parent || !depth || !bitmask || !pos ||
+      !num_nodes)
+    return tv::fail(TV_ERR_INVALID_ARG, "null pointer");
+  if (tree_off[0] != 0 || path_off[0] != 0)
+    return tv::fail(TV_ERR_INVALID_ARG, "tree_off[0] and path_off[0] must be 0");
+  if (!ranks && path_off[tree_off[B]] > 0) return tv::fail(TV_ERR_INVALID_ARG, "ranks is null");
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t p0 = tree_off[b], p1 = tree_off[b + 1];
+    if (p1 < p0) return tv::fail(TV_ERR_INVALID_ARG, "tree_off is not non-decreasing");
+    if (!prefix_ok(prefix_len[b])) {
+      if (bad_tree) *bad_tree = b;
+      return tv::fail(TV_ERR_INVALID_ARG, "prefix_len out of range");
+    }
+    const size_t row = static_cast<size_t>(b) * N;
+    int32_t n = 0, bad = -1;
+    const tv_status st = build_one(ranks, path_off, p0, p1, prefix_len[b], N, parent + row,
+                                   depth + row, bitmask + row, pos + row, &n, &bad);
+    if (st != TV_OK) {
+      if (bad_tree) *bad_tree = b;
+      if (bad_path) *bad_path = bad;
+      return st;
+    }
+    num_nodes[b] = n;
+    for (int32_t i = n; i < N; ++i) {  // padding leaves under the root
+      parent[row + i] = 0;
+      depth[row + i] = 1;
+      bitmask[row + i] = 1ull | (1ull << i);
+      pos[row + i] = prefix_len[b] + 1;
+    }
+  }
   return TV_OK;
 }
