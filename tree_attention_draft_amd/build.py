@@ -24,6 +24,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
           # packed fp32 instructions are kept out of every kernel on purpose
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-function",
+          # the direct-load asm clobbers M0 on purpose (the compiler re-sets it before use)
+          "-Wno-inline-asm",
           "-I", INCLUDE, "-I", CSRC]
 
 

@@ -51,14 +51,15 @@ int device_cu_count() {
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
-MfmaShape pick_mfma_shape(int qt, int* row_chunks) {
-  *row_chunks = 1;
-  if (qt <= 4) return MfmaShape{1, qt};
-  if (qt <= 8) return MfmaShape{2, (qt + 1) / 2};
-  if (qt <= 12) return MfmaShape{3, (qt + 2) / 3};
-  if (qt <= 16) return MfmaShape{4, (qt + 3) / 4};
-  *row_chunks = (qt + 31) / 32;
-  return MfmaShape{4, 8};
+// One wave per query head of the kv head's group (rounded up to a power of two, at most
+// 8 waves; larger groups take several head chunks), each wave owning all ceil(N/16)
+// 16-node tiles of its head.
+MfmaShape pick_mfma_shape(int N, int g, int* head_chunks) {
+  const int tn = (N + 15) / 16;
+  int nw = 1;
+  while (nw < g && nw < 8) nw *= 2;
+  *head_chunks = (g + nw - 1) / nw;
+  return MfmaShape{tn, nw};
 }
 
 tv_status check_args(const tv_attn_args* a, bool pointers) {
@@ -113,9 +114,8 @@ tv_status make_plan(const tv_attn_args* a, Plan* pl) {
   const bool bf16 = a->dtype == TV_BF16;
   pl->mfma = a->path == TV_PATH_MFMA || (a->path == TV_PATH_AUTO && bf16 && R >= 16);
   if (pl->mfma) {
-    const int qt = (R + 15) / 16;
-    pl->shape = pick_mfma_shape(qt, &pl->row_chunks);
-    pl->rows_per_wg = pl->shape.tpw * pl->shape.nw * 16;
+    pl->shape = pick_mfma_shape(a->N, g, &pl->row_chunks);
+    pl->rows_per_wg = pl->shape.nw * a->N;
   } else {
     pl->rows_per_wg = kValuRowsPerWg;
     pl->row_chunks = (R + kValuRowsPerWg - 1) / kValuRowsPerWg;
@@ -133,6 +133,12 @@ tv_status make_plan(const tv_attn_args* a, Plan* pl) {
     S = pairs >= target ? 1 : std::min<int64_t>(tiles, (target + pairs - 1) / pairs);
   }
   S = std::max<int64_t>(S, 1);
+  if (pl->mfma && a->kv_layout == TV_KV_PAGED) {
+    // a split's page-table slice must fit the kernel's LDS copy
+    const int64_t max_keys = (int64_t)(kMaxPageSlice - 1) * a->page_size;
+    const int64_t max_tiles = std::max<int64_t>(1, max_keys / kKeysPerTile);
+    S = std::max<int64_t>(S, (tiles + max_tiles - 1) / max_tiles);
+  }
   const int64_t chunk_tiles = (tiles + S - 1) / S;
   S = (tiles + chunk_tiles - 1) / chunk_tiles;
   pl->splits = (int)S;

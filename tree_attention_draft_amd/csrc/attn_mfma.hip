@@ -1,43 +1,133 @@
 // Tree-verify attention, MFMA path (bf16 inputs, fp32 accumulation, gfx950).
 //
 // Semantics ("Tree attention mask for draft-tree verification", "A strong answer";
-// "Tree Verification", "Tree Attention"): packed row r = node * g + j (g = Hq/Hkv) is query
-// head hkv*g + j of tree node r / g; it attends every prefix key t < L and tree key L + i
-// exactly when bit i of the node's ancestor bitmask is set.  The bitmask is built in LDS
-// from the parent array once per workgroup and expanded per key tile; prefix tiles carry
-// no mask at all.
+// "Tree Verification", "Tree Attention"): query head j of the kv head's group, at tree node
+// i, attends every prefix key t < L and tree key L + a exactly when a is i or an ancestor
+// of i.  The ancestor bitmask is built in LDS from the parent array once per workgroup
+// and turned into one 64-bit "allowed" word per row per key tile; tiles that hold only
+// prefix keys carry no mask at all.
 //
-// Work decomposition.  One workgroup = (key split, kv head [x row chunk], request).  All
-// N*g query rows of the kv head are packed node-major and cut into 16-row tiles; wave w
-// owns TPW consecutive tiles.  Each 64-key tile of K and V is read from HBM once per
-// workgroup, staged in LDS, and reused by every wave, i.e. by all heads and nodes of the
-// group.
+// Work decomposition.  One workgroup = (key split, kv head x head chunk, request) with NW
+// waves; wave w owns query head j = chunk*NW + w of the group and all its TN 16-node tiles,
+// so every wave does the same amount of work.  Each 64-key tile of K and V is read from
+// HBM once per workgroup and reused by every head and node of the group.
+//
+// Memory pipeline.  K and V tiles are copied global -> LDS by direct loads
+// (global_load_lds, 16 bytes per lane) into an NST-stage ring: no registers are tied up in
+// flight, and tile t+NST-1 is loading while tile t is computed.  One barrier per tile both
+// publishes tile t and frees the stage of tile t-1.  LDS rows are XOR-swizzled per 16-byte
+// chunk: K by (row mod 8) so the 16-byte operand reads of 8 consecutive rows hit distinct
+// banks; V by 2*(row mod 4) so the transposed reads of 4 consecutive rows do.
 //
 // Matrix-core layout (v_mfma_f32_16x16x32_bf16; lane l, lr = l % 16, lh = l / 16):
 //   A operand: row lr, k = 8*lh .. 8*lh+7;  B operand: column lr, same k;
 //   result:    rows 4*lh .. 4*lh+3 of column lr.
-// Scores are computed transposed, S^T = K Q^T (A = K tile from LDS, B = Q from registers),
-// so every lane holds 4 keys of ONE query row: the row max / sum are in-lane plus two
-// cross-lane steps.  The output is accumulated transposed too, O^T += V^T P^T: the P
-// values a lane owns (keys 4lh..4lh+3 of two 16-key blocks) are exactly a B operand once
-// the contraction index is permuted consistently, so P never leaves registers; V is
-// stored transposed in LDS so the matching A operand is two 8-byte reads.
+// Scores are computed transposed, S^T = K Q^T (A = K from LDS, B = Q in registers): a lane
+// holds 4 keys of ONE query row, so the row max is in-lane plus two cross-lane steps and
+// the row sum stays per lane until the end.  The output is accumulated transposed too,
+// O^T += V^T P^T: the P values a lane owns (keys 4lh..4lh+3 of two 16-key blocks) form a
+// B operand once the contraction index is permuted the same way on both sides, so P never
+// leaves registers.  The matching A operand (V^T) comes straight from V's natural
+// row-major layout through the transposing LDS read ds_read_b64_tr_b16: within each
+// 16-lane group, lane s addresses V[base + s/4][d0 + 4*(s%4) ..] and output lane l receives
+// V[base + j][d0 + l] for j = 0..3.
 #include "kernels_common.h"
 
 namespace tv {
 
-template <int D, int TPW, int NW>
-__global__ void __launch_bounds__(NW * 64) tv_attn_mfma_kernel(AttnParams p) {
-  constexpr int KT = kKeysPerTile;  // 64
-  constexpr int NT = NW * 64;
-  constexpr int DS = D / 32;        // k-steps of Q.K^T
-  constexpr int DB = D / 16;        // 16-feature output blocks
-  constexpr int KPAD = D + 8;       // K row pitch in elements (+16 B against bank conflicts)
-  constexpr int VPAD = KT + 4;      // V^T row pitch in elements (+8 B)
-  constexpr int KCH = D / 8;        // 16-byte chunks per key row
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[KT * KPAD];
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[D * VPAD];
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+#define TV_LDS __attribute__((address_space(3)))
+
+// s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane l's
+// bytes land at LDS address lds + 16*l.  Written as inline asm on purpose: the compiler
+// cannot tell which LDS bytes such a copy writes, so when it sees one it drains every
+// outstanding load (vmcnt 0) before each barrier and LDS read, which would serialise the
+// ring.  Completion is tracked explicitly with wait_vmcnt instead.  M0 carries the LDS
+// address; the compiler sets M0 itself before any of its own uses.
+__device__ inline void lds_load16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds), "v"(g) : "memory", "m0");
+}
+
+template <int D, int KT, int NST, int TN, int NW>
+struct MfmaCfg {
+  static constexpr int DS = D / 32;             // k-steps of Q.K^T
+  static constexpr int DB = D / 16;             // 16-feature output blocks
+  static constexpr int ROWB = D * 2;            // bytes per K or V row
+  static constexpr int CH = D / 8;              // 16-byte chunks per row
+  static constexpr int TILEB = KT * ROWB;       // bytes of one K (or V) tile
+  static constexpr int STAGEB = 2 * TILEB;      // K tile then V tile
+  static constexpr int RPI = 1024 / ROWB;       // rows per 1 KB load instruction
+  static constexpr int LI = STAGEB / 1024;      // load instructions per tile
+  static constexpr int LPW = LI / NW;           // ... per wave
+  static constexpr int KB = KT / 16;            // 16-key blocks per tile
+  static constexpr int KS = KT / 32;            // 32-key steps of P.V
+  static_assert(LI % NW == 0, "load instructions must split evenly over the waves");
+  static_assert(KT % 32 == 0 && NST >= 2, "tile shape");
+};
+
+__device__ inline int swz_k(int r) { return r & 7; }
+__device__ inline int swz_v(int r) { return (r & 3) << 1; }
+
+// Where the rows of one request / kv head live.  Contiguous: row t at base + t*kv_st.
+// Paged: row t at base + page*kv_sb + (t % page_size)*kv_st with the page id taken from
+// the LDS copy of this workgroup's slice of the page table (first page `pbase`).
+struct RowMap {
+  int64_t head_off;  // element offset of (request, kv head) [contiguous] or kv head [paged]
+  const int32_t* pt; // LDS page-table slice (paged only)
+  int pbase;
+};
+
+__device__ inline int64_t row_offset(const AttnParams& p, const RowMap& rm, int t) {
+  if (!p.paged) return rm.head_off + (int64_t)t * p.kv_st;
+  int pi, slot;
+  if (p.page_shift >= 0) {
+    pi = t >> p.page_shift;
+    slot = t & (p.page_size - 1);
+  } else {
+    pi = t / p.page_size;
+    slot = t - pi * p.page_size;
+  }
+  return rm.head_off + (int64_t)rm.pt[pi - rm.pbase] * p.kv_sb + (int64_t)slot * p.kv_st;
+}
+
+// Issue the direct loads of the tile at logical key kt0 into the stage at LDS address
+// `stage`.  Rows at or past kend are redirected to key kend-1 (finite data, masked out
+// later), so every LDS slot of the stage is rewritten and no read leaves [0, kend).
+template <class C, int NW>
+__device__ inline void issue_tile(const AttnParams& p, const RowMap& rm, const char* kg,
+                                  const char* vg, uint32_t stage, int kt0, int kend, int w,
+                                  int lane) {
+#pragma unroll
+  for (int ii = 0; ii < C::LPW; ++ii) {
+    const int i = ii * NW + w;                  // wave-uniform instruction index
+    const bool is_v = i >= C::LI / 2;
+    const int ik = is_v ? i - C::LI / 2 : i;
+    const int r = ik * C::RPI + lane / C::CH;
+    const int pp = lane % C::CH;
+    const int c = pp ^ (is_v ? swz_v(r) : swz_k(r));
+    const int t = min(kt0 + r, kend - 1);
+    const char* src = (is_v ? vg : kg) + row_offset(p, rm, t) * 2 + c * 16;
+    const uint32_t dst = stage + (is_v ? C::TILEB : 0) + ik * 1024;
+    lds_load16(src, __builtin_amdgcn_readfirstlane(dst));
+  }
+}
+
+template <int D, int KT, int NST, int TN, int NW>
+__global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) {
+  using C = MfmaCfg<D, KT, NST, TN, NW>;
+  constexpr int DS = C::DS, DB = C::DB, KB = C::KB, KS = C::KS;
+  __shared__ __attribute__((aligned(1024))) char smem[NST * C::STAGEB];
   __shared__ uint64_t mask_s[TV_MAX_NODES];
+  __shared__ int32_t pt_s[kMaxPageSlice];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -46,39 +136,38 @@ __global__ void __launch_bounds__(NW * 64) tv_attn_mfma_kernel(AttnParams p) {
   const int lh = lane >> 4;
   const int split = blockIdx.x;
   const int hkv = blockIdx.y % p.Hkv;
-  const int rc = blockIdx.y / p.Hkv;
+  const int hc = blockIdx.y / p.Hkv;
   const int b = blockIdx.z;
   const int L = clamped_prefix(p, b);
   const int Ttot = L + p.N;
   const int kbeg = split * p.chunk;
   if (kbeg >= Ttot) return;  // this request has fewer splits than the grid
   const int kend = min(kbeg + p.chunk, Ttot);
+  const int ntiles = (kend - kbeg + KT - 1) / KT;
 
-  const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(p.q);
-  const uint16_t* __restrict__ kg = static_cast<const uint16_t*>(p.k);
-  const uint16_t* __restrict__ vg = static_cast<const uint16_t*>(p.v);
+  const char* kg = static_cast<const char*>(p.k);
+  const char* vg = static_cast<const char*>(p.v);
+  const uint32_t sbase = (uint32_t)(uintptr_t)(TV_LDS char*)smem;
 
-  if (tid < p.N) {
-    bool ok;
-    int dd;
-    mask_s[tid] = ancestor_bits(p.parent + (int64_t)b * p.parent_sb, tid, p.N, ok, dd);
-  }
+  // ---- prologue: every compiler-visible global load (Q, parent array, page-table slice)
+  // happens here and is drained by one explicit wait before the asm-issued ring starts;
+  // otherwise the compiler would guard later uses of these registers with vmcnt(0) and
+  // drain the ring on every tile.
 
-  // ---- this wave's query tiles, as B operands (column = packed row, k = feature) ----
-  const int qt0 = (rc * NW + w) * TPW;  // first 16-row tile of this wave
-  bf16x8 qreg[TPW][DS];
-  int row_node[TPW];
-  bool tile_on[TPW];
+  // this wave's query head and node tiles, as B operands
+  const int j = hc * NW + w;              // query head within the kv head's group
+  const bool head_on = j < p.g;           // wave-uniform
+  const int head = hkv * p.g + (head_on ? j : 0);
+  bf16x8 qreg[TN][DS];
+  bool tile_on[TN];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int row = (qt0 + t) * 16 + lr;
-    tile_on[t] = (qt0 + t) * 16 < p.R;  // wave-uniform
-    const bool valid = row < p.R;
-    const int node = valid ? row / p.g : 0;
-    const int head = hkv * p.g + (valid ? row % p.g : 0);
-    row_node[t] = node;
-    const uint16_t* src = qg + (int64_t)b * p.q_sb + (int64_t)node * p.q_sn +
-                          (int64_t)head * p.q_sh + 8 * lh;
+  for (int t = 0; t < TN; ++t) {
+    const int node = t * 16 + lr;
+    tile_on[t] = head_on && t * 16 < p.N;  // wave-uniform
+    const bool valid = head_on && node < p.N;
+    const uint16_t* src = static_cast<const uint16_t*>(p.q) + (int64_t)b * p.q_sb +
+                          (int64_t)(valid ? node : 0) * p.q_sn + (int64_t)head * p.q_sh +
+                          8 * lh;
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
       uint4 v = make_uint4(0, 0, 0, 0);
@@ -87,68 +176,71 @@ __global__ void __launch_bounds__(NW * 64) tv_attn_mfma_kernel(AttnParams p) {
     }
   }
 
-  f32x4 o[TPW][DB];
-  float m[TPW], l[TPW];
+  if (tid < p.N) {
+    bool ok;
+    int dd;
+    mask_s[tid] = ancestor_bits(p.parent + (int64_t)b * p.parent_sb, tid, p.N, ok, dd);
+  }
+
+  RowMap rm;
+  rm.pt = pt_s;
+  rm.pbase = 0;
+  if (p.paged) {
+    // this split's slice of the page table, staged once in LDS (the host bounds its size)
+    rm.head_off = (int64_t)hkv * p.kv_sh;
+    rm.pbase = p.page_shift >= 0 ? (kbeg >> p.page_shift) : kbeg / p.page_size;
+    const int plast = p.page_shift >= 0 ? ((kend - 1) >> p.page_shift) : (kend - 1) / p.page_size;
+    const int32_t* prow = p.page_table + (int64_t)b * p.pages_per_seq;
+    for (int i = tid; i <= plast - rm.pbase; i += NW * 64) pt_s[i] = prow[rm.pbase + i];
+  } else {
+    rm.head_off = (int64_t)b * p.kv_sb + (int64_t)hkv * p.kv_sh;
+  }
+  wait_vmcnt<0>();
+  __syncthreads();  // mask_s and pt_s visible
+
+  // ---- start the first NST-1 tiles streaming ----
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < ntiles)
+      issue_tile<C, NW>(p, rm, kg, vg, sbase + s * C::STAGEB, kbeg + s * KT, kend, w, lane);
+
+  f32x4 o[TN][DB];
+  float m[TN], l[TN];
+#pragma unroll
+  for (int t = 0; t < TN; ++t) {
     m[t] = -INFINITY;
     l[t] = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[t][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  __syncthreads();  // mask_s ready
-  uint64_t rmask[TPW];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) rmask[t] = mask_s[row_node[t]];
-
   const float c = p.scale_log2;
 
-  for (int kt0 = kbeg; kt0 < kend; kt0 += KT) {
-    // ---- stage K (row-major) and V (transposed) for keys [kt0, kt0 + 64) in LDS ----
-    for (int ci = tid; ci < KT * KCH; ci += NT) {
-      const int key = ci / KCH, ch = ci - (ci / KCH) * KCH;
-      const int t = kt0 + key;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (t < kend) v = *reinterpret_cast<const uint4*>(kg + kv_offset(p, b, t, hkv) + 8 * ch);
-      *reinterpret_cast<uint4*>(&Ks[key * KPAD + 8 * ch]) = v;
-    }
-    for (int ui = tid; ui < (KT / 4) * KCH; ui += NT) {
-      const int kq = ui / KCH, ch = ui - (ui / KCH) * KCH;
-      uint4 r[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = kt0 + 4 * kq + e;
-        r[e] = make_uint4(0, 0, 0, 0);
-        if (t < kend) r[e] = *reinterpret_cast<const uint4*>(vg + kv_offset(p, b, t, hkv) + 8 * ch);
-      }
-      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r[0]);
-      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r[1]);
-      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r[2]);
-      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r[3]);
-#pragma unroll
-      for (int wi = 0; wi < 4; ++wi) {
-        uint2 even, odd;  // features 2*wi and 2*wi+1 of the four keys
-        even.x = (w0[wi] & 0xFFFFu) | (w1[wi] << 16);
-        even.y = (w2[wi] & 0xFFFFu) | (w3[wi] << 16);
-        odd.x = (w0[wi] >> 16) | (w1[wi] & 0xFFFF0000u);
-        odd.y = (w2[wi] >> 16) | (w3[wi] & 0xFFFF0000u);
-        const int d0 = 8 * ch + 2 * wi;
-        *reinterpret_cast<uint2*>(&Vt[d0 * VPAD + 4 * kq]) = even;
-        *reinterpret_cast<uint2*>(&Vt[(d0 + 1) * VPAD + 4 * kq]) = odd;
-      }
-    }
-    __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const int kt0 = kbeg + it * KT;
+    // my loads of tile `it` are complete once at most (tiles issued after it) x LPW remain
+    if (it + NST - 2 < ntiles) wait_vmcnt<(NST - 2) * C::LPW>();
+    else wait_vmcnt<0>();
+    __syncthreads();  // tile `it` visible to all waves; the stage of tile it-1 is free
+    if (it + NST - 1 < ntiles)
+      issue_tile<C, NW>(p, rm, kg, vg, sbase + ((it + NST - 1) % NST) * C::STAGEB,
+                        kt0 + (NST - 1) * KT, kend, w, lane);
+    if (!head_on) continue;  // surplus wave of a group smaller than NW: loads only
 
-    // ---- S^T = K Q^T for this wave's tiles ----
-    f32x4 sacc[TPW][4];
+    const char* ks = smem + (it % NST) * C::STAGEB;
+    const char* vs = ks + C::TILEB;
+
+    // ---- S^T = K Q^T ----
+    f32x4 sacc[TN][KB];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
+      const int r = kb * 16 + lr;
       bf16x8 ka[DS];
 #pragma unroll
       for (int s = 0; s < DS; ++s)
-        ka[s] = *reinterpret_cast<const bf16x8*>(&Ks[(kb * 16 + lr) * KPAD + 32 * s + 8 * lh]);
+        ka[s] = *reinterpret_cast<const bf16x8*>(ks + r * C::ROWB +
+                                                 (((4 * s + lh) ^ swz_k(r)) << 4));
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) {
+      for (int t = 0; t < TN; ++t) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
         if (tile_on[t]) {
 #pragma unroll
@@ -159,24 +251,23 @@ __global__ void __launch_bounds__(NW * 64) tv_attn_mfma_kernel(AttnParams p) {
       }
     }
 
-    // ---- mask (tree tail only), online softmax, P packing ----
-    // Lane (lr, lh) holds keys kt0 + 16*kb + 4*lh + i of its row: bit 16*kb + i of the
-    // tile's allowed word shifted down by 4*lh.
+    // ---- tree-tail mask, online softmax, P packing ----
     const bool masked = kt0 + KT > L;
-    bf16x8 pk[TPW][2];
+    bf16x8 pk[TN][KS];
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
+    for (int t = 0; t < TN; ++t) {
       if (masked) {
-        const uint64_t allow = tile_allowed(rmask[t], kt0, L) >> (4 * lh);
+        const int node = min(t * 16 + lr, p.N - 1);
+        const uint64_t allow = tile_allowed(mask_s[node], kt0, L) >> (4 * lh);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             sacc[t][kb][i] = ((allow >> (16 * kb + i)) & 1ull) ? sacc[t][kb][i] : -INFINITY;
       }
       float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[t][kb][i]);
       mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -187,7 +278,7 @@ __global__ void __launch_bounds__(NW * 64) tv_attn_mfma_kernel(AttnParams p) {
       m[t] = m_new;
       float rs = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float e = __builtin_amdgcn_exp2f(fmaf(sacc[t][kb][i], c, -m_use));
@@ -204,34 +295,41 @@ __global__ void __launch_bounds__(NW * 64) tv_attn_mfma_kernel(AttnParams p) {
       }
     }
 
-    // ---- O^T += V^T P^T ----
+    // ---- O^T += V^T P^T, V^T read transposed from V's row-major tile ----
+    const int q4 = lr & 3;                       // which 4-feature group this lane addresses
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
+      const int chunk = 2 * db + (q4 >> 1);      // 16-byte chunk of features 16db + 4q4
+      const int half = (q4 & 1) << 3;            // byte offset inside the chunk
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const __bf16* base = &Vt[(db * 16 + lr) * VPAD + 32 * ks + 4 * lh];
-        const uint2 lo = *reinterpret_cast<const uint2*>(base);
-        const uint2 hi = *reinterpret_cast<const uint2*>(base + 16);
-        const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+      for (int kss = 0; kss < KS; ++kss) {
+        const int r0 = 32 * kss + 4 * lh + (lr >> 2);
+        const int r1 = r0 + 16;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (TV_LDS v4i16*)(vs + r0 * C::ROWB + ((chunk ^ swz_v(r0)) << 4) + half));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (TV_LDS v4i16*)(vs + r1 * C::ROWB + ((chunk ^ swz_v(r1)) << 4) + half));
+        const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 va = __builtin_bit_cast(bf16x8, both);
 #pragma unroll
-        for (int t = 0; t < TPW; ++t)
+        for (int t = 0; t < TN; ++t)
           if (tile_on[t])
-            o[t][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pk[t][ks], o[t][db], 0, 0, 0);
+            o[t][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pk[t][kss], o[t][db], 0, 0, 0);
       }
     }
-    __syncthreads();  // LDS tile consumed before the next one is staged
   }
 
+  if (!head_on) return;
   // ---- epilogue: normalise and store (final output, or split partials) ----
   const bool single = p.num_splits == 1;
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
+  for (int t = 0; t < TN; ++t) {
     float lt = l[t];
     lt += __shfl_xor(lt, 16);
     lt += __shfl_xor(lt, 32);
-    const int row = (qt0 + t) * 16 + lr;
-    if (!tile_on[t] || row >= p.R) continue;
-    const int node = row / p.g, head = hkv * p.g + row % p.g;
+    const int node = t * 16 + lr;
+    if (!tile_on[t] || node >= p.N) continue;
+    const int row = node * p.g + j;  // packed row (node-major) of the split workspace
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const float lse2 = lt > 0.f ? m[t] + log2f(lt) : -INFINITY;
     if (single) {
@@ -256,18 +354,22 @@ __global__ void __launch_bounds__(NW * 64) tv_attn_mfma_kernel(AttnParams p) {
   }
 }
 
+constexpr int kMfmaKT = 32;
+constexpr int kMfmaNST = 4;
+
 template <int D>
 static hipError_t launch_d(const AttnParams& p, MfmaShape sh, hipStream_t s) {
   dim3 grid(p.num_splits, p.Hkv * p.row_chunks, p.B);
-#define TV_CASE(TPW, NW)                                                             \
-  if (sh.tpw == TPW && sh.nw == NW) {                                                \
-    hipLaunchKernelGGL((tv_attn_mfma_kernel<D, TPW, NW>), grid, dim3(NW * 64), 0, s, p); \
-    return hipGetLastError();                                                        \
+#define TV_CASE(TN, NW)                                                                   \
+  if (sh.tpw == TN && sh.nw == NW) {                                                      \
+    hipLaunchKernelGGL((tv_attn_mfma_kernel<D, kMfmaKT, kMfmaNST, TN, NW>), grid,         \
+                       dim3(NW * 64), 0, s, p);                                           \
+    return hipGetLastError();                                                             \
   }
-  TV_CASE(1, 1) TV_CASE(1, 2) TV_CASE(1, 3) TV_CASE(1, 4)
-  TV_CASE(2, 3) TV_CASE(2, 4)
-  TV_CASE(3, 3) TV_CASE(3, 4)
-  TV_CASE(4, 3) TV_CASE(4, 4) TV_CASE(4, 8)
+  TV_CASE(1, 1) TV_CASE(1, 2) TV_CASE(1, 4) TV_CASE(1, 8)
+  TV_CASE(2, 1) TV_CASE(2, 2) TV_CASE(2, 4) TV_CASE(2, 8)
+  TV_CASE(3, 1) TV_CASE(3, 2) TV_CASE(3, 4) TV_CASE(3, 8)
+  TV_CASE(4, 1) TV_CASE(4, 2) TV_CASE(4, 4) TV_CASE(4, 8)
 #undef TV_CASE
   return hipErrorInvalidConfiguration;
 }

@@ -11,7 +11,8 @@ namespace tv {
 // Records a detail string for tv_last_error() on this thread and returns `s`.
 tv_status fail(tv_status s, const char* detail);
 
-constexpr int kKeysPerTile = 64;  // keys staged in LDS per step of the streaming loop
+constexpr int kKeysPerTile = 64;  // split chunks are multiples of this many keys
+constexpr int kMaxPageSlice = 1024;  // page-table entries one MFMA workgroup stages in LDS
 
 // Everything a kernel needs, passed by value.  Strides in elements.
 struct AttnParams {
@@ -35,12 +36,13 @@ struct AttnParams {
   int32_t B, N, Hq, Hkv, g, R;
   int32_t num_splits;  // S
   int32_t chunk;       // keys per split, a multiple of kKeysPerTile
-  int32_t row_chunks;  // workgroups along the packed-row dimension
+  int32_t row_chunks;  // workgroups along the packed-row (MFMA: query-head) dimension
   int32_t rows_per_wg; // packed rows one workgroup covers
   float scale_log2;    // sm_scale * log2(e)
 };
 
-// MFMA kernel shape: each wave owns `tpw` 16-row tiles; `nw` waves per workgroup.
+// MFMA kernel shape: `nw` waves per workgroup, one query head each; every wave owns
+// `tpw` = ceil(N/16) tiles of 16 tree nodes.
 struct MfmaShape {
   int tpw, nw;
 };
