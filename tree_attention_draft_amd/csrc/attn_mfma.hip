@@ -16,8 +16,7 @@
 // (global_load_lds, 16 bytes per lane) into an NST-stage ring: no registers are tied up in
 // flight, and tile t+NST-1 is loading while tile t is computed.  One barrier per tile both
 // publishes tile t and frees the stage of tile t-1.  LDS rows are XOR-swizzled per 16-byte
-// chunk: K by (row mod 8) so the 16-byte operand reads of 8 consecutive rows hit distinct
-// banks; V by 2*(row mod 4) so the transposed reads of 4 consecutive rows do.
+// chunk (K by row, V by row pairs; see swz_k / swz_v) so operand reads are conflict-free.
 //
 // Matrix-core layout (v_mfma_f32_16x16x32_bf16; lane l, lr = l % 16, lh = l / 16):
 //   A operand: row lr, k = 8*lh .. 8*lh+7;  B operand: column lr, same k;
@@ -54,8 +53,11 @@ __device__ inline void wait_vmcnt() {
 // address; the compiler sets M0 itself before any of its own uses.
 __device__ inline void lds_load16(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(lds), "v"(g) : "memory", "m0");
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(g) : "memory", "m0");
 }
+
+// Online-softmax rebasing threshold in log2 units (see the softmax step of the kernel).
+constexpr float kRebase = 8.f;
 
 template <int D, int KT, int NST, int TN, int NW>
 struct MfmaCfg {
@@ -74,8 +76,14 @@ struct MfmaCfg {
   static_assert(KT % 32 == 0 && NST >= 2, "tile shape");
 };
 
-__device__ inline int swz_k(int r) { return r & 7; }
-__device__ inline int swz_v(int r) { return (r & 3) << 1; }
+// XOR swizzles of the 16-byte chunk index, period = the whole row (CH chunks): K rows by
+// row mod CH, so the 16-byte operand reads of any 16 consecutive rows hit distinct banks;
+// V rows by 2*(row mod CH/2), so the 32-byte transposed-read segments of any 8
+// consecutive rows do.
+template <int CH>
+__device__ inline int swz_k(int r) { return r & (CH - 1); }
+template <int CH>
+__device__ inline int swz_v(int r) { return (r & (CH / 2 - 1)) << 1; }
 
 // Where the rows of one request / kv head live.  Contiguous: row t at base + t*kv_st.
 // Paged: row t at base + page*kv_sb + (t % page_size)*kv_st with the page id taken from
@@ -99,25 +107,53 @@ __device__ inline int64_t row_offset(const AttnParams& p, const RowMap& rm, int 
   return rm.head_off + (int64_t)rm.pt[pi - rm.pbase] * p.kv_sb + (int64_t)slot * p.kv_st;
 }
 
-// Issue the direct loads of the tile at logical key kt0 into the stage at LDS address
-// `stage`.  Rows at or past kend are redirected to key kend-1 (finite data, masked out
-// later), so every LDS slot of the stage is rewritten and no read leaves [0, kend).
+// Per-wave load assignment: instruction ii of a tile copies 1 KB = RPI rows of K (first
+// half of the instructions) or V (second half) into the stage.  For each instruction a lane
+// owns one 16-byte chunk: row r, LDS position lane % CH, global chunk swizzled.
 template <class C, int NW>
-__device__ inline void issue_tile(const AttnParams& p, const RowMap& rm, const char* kg,
-                                  const char* vg, uint32_t stage, int kt0, int kend, int w,
-                                  int lane) {
+struct LoadPlan {
+  int r[C::LPW];          // row within the tile
+  int coff[C::LPW];       // byte offset of the (swizzled) global chunk within the row
+  bool is_v[C::LPW];      // wave-uniform
+  uint32_t dst[C::LPW];   // LDS byte offset within a stage (wave-uniform)
+  const char* src0[C::LPW];  // contiguous KV: address of row r of the tile at key 0
+
+  __device__ LoadPlan(const AttnParams& p, const RowMap& rm, const char* kg, const char* vg,
+                      int w, int lane) {
+#pragma unroll
+    for (int ii = 0; ii < C::LPW; ++ii) {
+      const int i = ii * NW + w;
+      is_v[ii] = i >= C::LI / 2;
+      const int ik = is_v[ii] ? i - C::LI / 2 : i;
+      r[ii] = ik * C::RPI + lane / C::CH;
+      const int c = (lane % C::CH) ^ (is_v[ii] ? swz_v<C::CH>(r[ii]) : swz_k<C::CH>(r[ii]));
+      coff[ii] = c * 16;
+      dst[ii] = (is_v[ii] ? C::TILEB : 0) + ik * 1024;
+      src0[ii] = (is_v[ii] ? vg : kg) + (rm.head_off + (int64_t)r[ii] * p.kv_st) * 2 + coff[ii];
+    }
+  }
+};
+
+// Issue the direct loads of the tile at logical key kt0 into the stage at LDS address
+// `stage`.  Full tiles of contiguous KV only add a uniform advance to precomputed
+// addresses.  Otherwise (paged KV, or the last, partial tile) rows at or past kend are
+// redirected to key kend-1 (finite data, masked out later), so every LDS slot of the stage
+// is rewritten and no read leaves [0, kend).
+template <class C, int NW, int KT>
+__device__ inline void issue_tile(const AttnParams& p, const RowMap& rm,
+                                  const LoadPlan<C, NW>& lp, const char* kg, const char* vg,
+                                  uint32_t stage, int kt0, int kend) {
+  if (!p.paged && kt0 + KT <= kend) {
+    const int64_t adv = (int64_t)kt0 * p.kv_st * 2;
+#pragma unroll
+    for (int ii = 0; ii < C::LPW; ++ii) lds_load16(lp.src0[ii] + adv, stage + lp.dst[ii]);
+    return;
+  }
 #pragma unroll
   for (int ii = 0; ii < C::LPW; ++ii) {
-    const int i = ii * NW + w;                  // wave-uniform instruction index
-    const bool is_v = i >= C::LI / 2;
-    const int ik = is_v ? i - C::LI / 2 : i;
-    const int r = ik * C::RPI + lane / C::CH;
-    const int pp = lane % C::CH;
-    const int c = pp ^ (is_v ? swz_v(r) : swz_k(r));
-    const int t = min(kt0 + r, kend - 1);
-    const char* src = (is_v ? vg : kg) + row_offset(p, rm, t) * 2 + c * 16;
-    const uint32_t dst = stage + (is_v ? C::TILEB : 0) + ik * 1024;
-    lds_load16(src, __builtin_amdgcn_readfirstlane(dst));
+    const int t = min(kt0 + lp.r[ii], kend - 1);
+    const char* src = (lp.is_v[ii] ? vg : kg) + row_offset(p, rm, t) * 2 + lp.coff[ii];
+    lds_load16(src, stage + lp.dst[ii]);
   }
 }
 
@@ -131,7 +167,7 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
   const int lr = lane & 15;
   const int lh = lane >> 4;
   const int split = blockIdx.x;
@@ -158,12 +194,12 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
   const int j = hc * NW + w;              // query head within the kv head's group
   const bool head_on = j < p.g;           // wave-uniform
   const int head = hkv * p.g + (head_on ? j : 0);
+  // TN = ceil(N/16), so every node tile holds at least one real node; rows past N are
+  // zero queries whose results are never stored.
   bf16x8 qreg[TN][DS];
-  bool tile_on[TN];
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
     const int node = t * 16 + lr;
-    tile_on[t] = head_on && t * 16 < p.N;  // wave-uniform
     const bool valid = head_on && node < p.N;
     const uint16_t* src = static_cast<const uint16_t*>(p.q) + (int64_t)b * p.q_sb +
                           (int64_t)(valid ? node : 0) * p.q_sn + (int64_t)head * p.q_sh +
@@ -199,10 +235,11 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
   __syncthreads();  // mask_s and pt_s visible
 
   // ---- start the first NST-1 tiles streaming ----
+  const LoadPlan<C, NW> lp(p, rm, kg, vg, w, lane);
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)
     if (s < ntiles)
-      issue_tile<C, NW>(p, rm, kg, vg, sbase + s * C::STAGEB, kbeg + s * KT, kend, w, lane);
+      issue_tile<C, NW, KT>(p, rm, lp, kg, vg, sbase + s * C::STAGEB, kbeg + s * KT, kend);
 
   f32x4 o[TN][DB];
   float m[TN], l[TN];
@@ -222,8 +259,8 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
     else wait_vmcnt<0>();
     __syncthreads();  // tile `it` visible to all waves; the stage of tile it-1 is free
     if (it + NST - 1 < ntiles)
-      issue_tile<C, NW>(p, rm, kg, vg, sbase + ((it + NST - 1) % NST) * C::STAGEB,
-                        kt0 + (NST - 1) * KT, kend, w, lane);
+      issue_tile<C, NW, KT>(p, rm, lp, kg, vg, sbase + ((it + NST - 1) % NST) * C::STAGEB,
+                            kt0 + (NST - 1) * KT, kend);
     if (!head_on) continue;  // surplus wave of a group smaller than NW: loads only
 
     const char* ks = smem + (it % NST) * C::STAGEB;
@@ -238,15 +275,13 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
 #pragma unroll
       for (int s = 0; s < DS; ++s)
         ka[s] = *reinterpret_cast<const bf16x8*>(ks + r * C::ROWB +
-                                                 (((4 * s + lh) ^ swz_k(r)) << 4));
+                                                 (((4 * s + lh) ^ swz_k<C::CH>(r)) << 4));
 #pragma unroll
       for (int t = 0; t < TN; ++t) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (tile_on[t]) {
 #pragma unroll
-          for (int s = 0; s < DS; ++s)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s], qreg[t][s], acc, 0, 0, 0);
-        }
+        for (int s = 0; s < DS; ++s)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s], qreg[t][s], acc, 0, 0, 0);
         sacc[t][kb] = acc;
       }
     }
@@ -265,17 +300,30 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
           for (int i = 0; i < 4; ++i)
             sacc[t][kb][i] = ((allow >> (16 * kb + i)) & 1ull) ? sacc[t][kb][i] : -INFINITY;
       }
+      // Lazy rebasing: a row keeps its reference max m until one of its scores exceeds
+      // it by more than kRebase (log2 units).  Each lane tests only its own scores; the
+      // row max over lanes and the O/l rescale run only when some lane trips the test,
+      // which after the first tile is rare.  Exponents stay <= kRebase, so P <= 2^kRebase
+      // (no overflow in fp32 or bf16) and the final division by l cancels the reference.
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[t][kb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m[t], mx * c);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m[t] - m_use);
-      m[t] = m_new;
+      mx *= c;
+      if (__any(mx > m[t] + kRebase)) {  // wave-uniform branch
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m[t], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m[t] - m_new);  // 0 when m was -inf
+        if (m_new != -INFINITY) {
+          l[t] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) o[t][db] *= alpha;
+          m[t] = m_new;
+        }
+      }
+      const float m_use = (m[t] == -INFINITY) ? 0.f : m[t];
       float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
@@ -286,13 +334,7 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
           pk[t][kb >> 1][(kb & 1) * 4 + i] = static_cast<__bf16>(e);
         }
       }
-      l[t] = fmaf(l[t], alpha, rs);
-      // the running max rarely moves after the first tiles: skip the rescale when no row
-      // of this wave changed (wave-uniform branch)
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o[t][db] *= alpha;
-      }
+      l[t] += rs;
     }
 
     // ---- O^T += V^T P^T, V^T read transposed from V's row-major tile ----
@@ -306,15 +348,14 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
         const int r0 = 32 * kss + 4 * lh + (lr >> 2);
         const int r1 = r0 + 16;
         const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (TV_LDS v4i16*)(vs + r0 * C::ROWB + ((chunk ^ swz_v(r0)) << 4) + half));
+            (TV_LDS v4i16*)(vs + r0 * C::ROWB + ((chunk ^ swz_v<C::CH>(r0)) << 4) + half));
         const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (TV_LDS v4i16*)(vs + r1 * C::ROWB + ((chunk ^ swz_v(r1)) << 4) + half));
+            (TV_LDS v4i16*)(vs + r1 * C::ROWB + ((chunk ^ swz_v<C::CH>(r1)) << 4) + half));
         const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         const bf16x8 va = __builtin_bit_cast(bf16x8, both);
 #pragma unroll
         for (int t = 0; t < TN; ++t)
-          if (tile_on[t])
-            o[t][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pk[t][kss], o[t][db], 0, 0, 0);
+          o[t][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pk[t][kss], o[t][db], 0, 0, 0);
       }
     }
   }
@@ -328,7 +369,7 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
     lt += __shfl_xor(lt, 16);
     lt += __shfl_xor(lt, 32);
     const int node = t * 16 + lr;
-    if (!tile_on[t] || node >= p.N) continue;
+    if (node >= p.N) continue;
     const int row = node * p.g + j;  // packed row (node-major) of the split workspace
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const float lse2 = lt > 0.f ? m[t] + log2f(lt) : -INFINITY;
