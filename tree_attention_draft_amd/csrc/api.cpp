@@ -52,14 +52,18 @@ int device_cu_count() {
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
 // One wave per query head of the kv head's group (rounded up to a power of two, at most
-// 8 waves; larger groups take several head chunks), each wave owning all ceil(N/16)
-// 16-node tiles of its head.
+// 8 waves; larger groups take several head chunks), each wave owning the head's 16-node
+// tiles.  When the nodes past the last full tile of all heads fit one 16-row tile (and the
+// group is exactly the waves of one workgroup), they are packed into a shared tile that
+// the waves take turns computing instead of padding every head's last tile.
 MfmaShape pick_mfma_shape(int N, int g, int* head_chunks) {
-  const int tn = (N + 15) / 16;
   int nw = 1;
   while (nw < g && nw < 8) nw *= 2;
   *head_chunks = (g + nw - 1) / nw;
-  return MfmaShape{tn, nw};
+  const int full = N / 16, rem = N % 16;
+  if (nw == g && g >= 2 && full >= 1 && full <= 3 && rem > 0 && rem * g <= 16)
+    return MfmaShape{full, nw, 1};
+  return MfmaShape{(N + 15) / 16, nw, 0};
 }
 
 tv_status check_args(const tv_attn_args* a, bool pointers) {

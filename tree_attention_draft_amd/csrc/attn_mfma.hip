@@ -157,13 +157,98 @@ __device__ inline void issue_tile(const AttnParams& p, const RowMap& rm,
   }
 }
 
-template <int D, int KT, int NST, int TN, int NW>
+// Online softmax of one 16-row x KT-key score tile held transposed (lane: 4 keys of one
+// row per 16-key block), with lazy rebasing: a row keeps its reference max m until one of
+// its scores exceeds it by more than kRebase (log2 units).  Each lane tests only its own
+// scores; the row max over lanes and the O/l rescale run only when some lane trips the
+// test, which after the first tile is rare.  Exponents stay <= kRebase, so P <= 2^kRebase
+// (no overflow in fp32 or bf16) and the final division by l cancels the reference.
+// `allow` (masked tiles only) holds this lane's allowed-key bits: bit 16*kb + i.
+template <int KB, int KS, int DB>
+__device__ inline void softmax_tile(f32x4 (&sacc)[KB], float& m, float& l, f32x4 (&o)[DB],
+                                    bf16x8 (&pk)[KS], float c, bool masked, uint64_t allow) {
+  if (masked) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sacc[kb][i] = ((allow >> (16 * kb + i)) & 1ull) ? sacc[kb][i] : -INFINITY;
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[kb][i]);
+  mx *= c;
+  if (__any(mx > m + kRebase)) {  // wave-uniform branch
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 when m was -inf
+    if (m_new != -INFINITY) {
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      m = m_new;
+    }
+  }
+  const float m_use = (m == -INFINITY) ? 0.f : m;
+  float rs = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, -m_use));
+      rs += e;
+      pk[kb >> 1][(kb & 1) * 4 + i] = static_cast<__bf16>(e);
+    }
+  }
+  l += rs;
+}
+
+// Final store of one row: normalised output and natural-log LSE, or the split partial.
+template <int D>
+__device__ inline void store_row_block(const AttnParams& p, int b, int hkv, int split,
+                                       int node, int head, int row, int lh,
+                                       const f32x4 (&o)[D / 16], float m, float lt) {
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float lse2 = lt > 0.f ? m + log2f(lt) : -INFINITY;
+  if (p.num_splits == 1) {
+    uint16_t* out = static_cast<uint16_t*>(p.out) + (int64_t)b * p.o_sb +
+                    (int64_t)node * p.o_sn + (int64_t)head * p.o_sh;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      bf16x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = static_cast<__bf16>(o[db][i] * inv);
+      *reinterpret_cast<bf16x4*>(out + db * 16 + 4 * lh) = v;
+    }
+    if (lh == 0 && p.lse) p.lse[((int64_t)b * p.N + node) * p.Hq + head] = lse2 * kLn2;
+  } else {
+    const int64_t prow = (((int64_t)b * p.Hkv + hkv) * p.num_splits + split) * p.R + row;
+    float* dst = p.ws_o + prow * D;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+      *reinterpret_cast<f32x4*>(dst + db * 16 + 4 * lh) = o[db] * inv;
+    if (lh == 0) p.ws_lse[prow] = lse2;
+  }
+}
+
+// TN full 16-node tiles per wave (wave w = query head w of the group).  RR = 1 adds the
+// shared remainder tile: the N - 16*TN nodes past the full tiles, packed node-major
+// across the g heads (row = (node - 16*TN) * g + head), computed by wave it % NW on key
+// tile `it`; each wave keeps its own online-softmax partial of that tile and the partials
+// are merged through LDS at the end (the same maths as the split merge).
+template <int D, int KT, int NST, int TN, int RR, int NW>
 __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) {
   using C = MfmaCfg<D, KT, NST, TN, NW>;
   constexpr int DS = C::DS, DB = C::DB, KB = C::KB, KS = C::KS;
+  constexpr int TT = TN + RR;  // tiles of state per wave: full tiles, then the shared one
   __shared__ __attribute__((aligned(1024))) char smem[NST * C::STAGEB];
   __shared__ uint64_t mask_s[TV_MAX_NODES];
   __shared__ int32_t pt_s[kMaxPageSlice];
+  static_assert(!RR || NW * 16 * D * 4 <= NST * C::STAGEB, "merge buffer fits the ring");
+  static_assert(!RR || NW * 16 * 2 <= kMaxPageSlice, "merge (m, l) fits the page slice");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -189,21 +274,29 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
   // happens here and is drained by one explicit wait before the asm-issued ring starts;
   // otherwise the compiler would guard later uses of these registers with vmcnt(0) and
   // drain the ring on every tile.
-
-  // this wave's query head and node tiles, as B operands
   const int j = hc * NW + w;              // query head within the kv head's group
   const bool head_on = j < p.g;           // wave-uniform
   const int head = hkv * p.g + (head_on ? j : 0);
-  // TN = ceil(N/16), so every node tile holds at least one real node; rows past N are
-  // zero queries whose results are never stored.
-  bf16x8 qreg[TN][DS];
+  const int rem_rows = RR ? (p.N - 16 * TN) * p.g : 0;  // valid rows of the shared tile
+  bf16x8 qreg[TT][DS];
+  int node_of[TT];  // tree node of this lane's row in each tile, clamped into [0, N)
 #pragma unroll
-  for (int t = 0; t < TN; ++t) {
-    const int node = t * 16 + lr;
-    const bool valid = head_on && node < p.N;
+  for (int t = 0; t < TT; ++t) {
+    int node, hd;
+    bool valid;
+    if (t < TN) {  // full tiles: head-major, every one holds at least one real node
+      node = t * 16 + lr;
+      hd = head;
+      valid = head_on && node < p.N;
+    } else {       // shared remainder tile: node-major across the group's heads
+      node = 16 * TN + lr / p.g;
+      hd = hkv * p.g + lr % p.g;
+      valid = head_on && lr < rem_rows;
+    }
+    node_of[t] = min(node, p.N - 1);
     const uint16_t* src = static_cast<const uint16_t*>(p.q) + (int64_t)b * p.q_sb +
-                          (int64_t)(valid ? node : 0) * p.q_sn + (int64_t)head * p.q_sh +
-                          8 * lh;
+                          (int64_t)(valid ? node : 0) * p.q_sn +
+                          (int64_t)(valid ? hd : 0) * p.q_sh + 8 * lh;
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
       uint4 v = make_uint4(0, 0, 0, 0);
@@ -241,10 +334,10 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
     if (s < ntiles)
       issue_tile<C, NW, KT>(p, rm, lp, kg, vg, sbase + s * C::STAGEB, kbeg + s * KT, kend);
 
-  f32x4 o[TN][DB];
-  float m[TN], l[TN];
+  f32x4 o[TT][DB];
+  float m[TT], l[TT];
 #pragma unroll
-  for (int t = 0; t < TN; ++t) {
+  for (int t = 0; t < TT; ++t) {
     m[t] = -INFINITY;
     l[t] = 0.f;
 #pragma unroll
@@ -262,12 +355,13 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
       issue_tile<C, NW, KT>(p, rm, lp, kg, vg, sbase + ((it + NST - 1) % NST) * C::STAGEB,
                             kt0 + (NST - 1) * KT, kend);
     if (!head_on) continue;  // surplus wave of a group smaller than NW: loads only
+    const bool do_rem = RR && (it % NW) == w;  // wave-uniform
 
     const char* ks = smem + (it % NST) * C::STAGEB;
     const char* vs = ks + C::TILEB;
 
     // ---- S^T = K Q^T ----
-    f32x4 sacc[TN][KB];
+    f32x4 sacc[TT][KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const int r = kb * 16 + lr;
@@ -277,7 +371,8 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
         ka[s] = *reinterpret_cast<const bf16x8*>(ks + r * C::ROWB +
                                                  (((4 * s + lh) ^ swz_k<C::CH>(r)) << 4));
 #pragma unroll
-      for (int t = 0; t < TN; ++t) {
+      for (int t = 0; t < TT; ++t) {
+        if (t >= TN && !do_rem) continue;
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < DS; ++s)
@@ -288,53 +383,12 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
 
     // ---- tree-tail mask, online softmax, P packing ----
     const bool masked = kt0 + KT > L;
-    bf16x8 pk[TN][KS];
+    bf16x8 pk[TT][KS];
 #pragma unroll
-    for (int t = 0; t < TN; ++t) {
-      if (masked) {
-        const int node = min(t * 16 + lr, p.N - 1);
-        const uint64_t allow = tile_allowed(mask_s[node], kt0, L) >> (4 * lh);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            sacc[t][kb][i] = ((allow >> (16 * kb + i)) & 1ull) ? sacc[t][kb][i] : -INFINITY;
-      }
-      // Lazy rebasing: a row keeps its reference max m until one of its scores exceeds
-      // it by more than kRebase (log2 units).  Each lane tests only its own scores; the
-      // row max over lanes and the O/l rescale run only when some lane trips the test,
-      // which after the first tile is rare.  Exponents stay <= kRebase, so P <= 2^kRebase
-      // (no overflow in fp32 or bf16) and the final division by l cancels the reference.
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[t][kb][i]);
-      mx *= c;
-      if (__any(mx > m[t] + kRebase)) {  // wave-uniform branch
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m[t], mx);
-        const float alpha = __builtin_amdgcn_exp2f(m[t] - m_new);  // 0 when m was -inf
-        if (m_new != -INFINITY) {
-          l[t] *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) o[t][db] *= alpha;
-          m[t] = m_new;
-        }
-      }
-      const float m_use = (m[t] == -INFINITY) ? 0.f : m[t];
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[t][kb][i], c, -m_use));
-          rs += e;
-          pk[t][kb >> 1][(kb & 1) * 4 + i] = static_cast<__bf16>(e);
-        }
-      }
-      l[t] += rs;
+    for (int t = 0; t < TT; ++t) {
+      if (t >= TN && !do_rem) continue;
+      const uint64_t allow = masked ? tile_allowed(mask_s[node_of[t]], kt0, L) >> (4 * lh) : 0ull;
+      softmax_tile<KB, KS, DB>(sacc[t], m[t], l[t], o[t], pk[t], c, masked, allow);
     }
 
     // ---- O^T += V^T P^T, V^T read transposed from V's row-major tile ----
@@ -354,43 +408,79 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
         const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         const bf16x8 va = __builtin_bit_cast(bf16x8, both);
 #pragma unroll
-        for (int t = 0; t < TN; ++t)
+        for (int t = 0; t < TT; ++t) {
+          if (t >= TN && !do_rem) continue;
           o[t][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pk[t][kss], o[t][db], 0, 0, 0);
+        }
       }
     }
   }
 
-  if (!head_on) return;
-  // ---- epilogue: normalise and store (final output, or split partials) ----
-  const bool single = p.num_splits == 1;
+  // ---- epilogue: full tiles straight from registers ----
+  if (head_on) {
 #pragma unroll
-  for (int t = 0; t < TN; ++t) {
-    float lt = l[t];
+    for (int t = 0; t < TN; ++t) {
+      float lt = l[t];
+      lt += __shfl_xor(lt, 16);
+      lt += __shfl_xor(lt, 32);
+      const int node = t * 16 + lr;
+      if (node < p.N)
+        store_row_block<D>(p, b, hkv, split, node, head, node * p.g + j, lh, o[t], m[t], lt);
+    }
+  }
+  if constexpr (RR) {
+    // ---- shared remainder tile: merge the waves' partials through LDS ----
+    float* mo = reinterpret_cast<float*>(smem);   // [NW][16][D] unnormalised O
+    float* ml = reinterpret_cast<float*>(pt_s);   // [NW][16] x (m, l)
+    __syncthreads();                              // every wave is done with the ring
+    float lt = l[TN];
     lt += __shfl_xor(lt, 16);
     lt += __shfl_xor(lt, 32);
-    const int node = t * 16 + lr;
-    if (node >= p.N) continue;
-    const int row = node * p.g + j;  // packed row (node-major) of the split workspace
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const float lse2 = lt > 0.f ? m[t] + log2f(lt) : -INFINITY;
-    if (single) {
-      uint16_t* out = static_cast<uint16_t*>(p.out) + (int64_t)b * p.o_sb +
-                      (int64_t)node * p.o_sn + (int64_t)head * p.o_sh;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < DB; ++db)
+      *reinterpret_cast<f32x4*>(mo + (w * 16 + lr) * D + db * 16 + 4 * lh) = o[TN][db];
+    if (lh == 0) {
+      ml[(w * 16 + lr) * 2] = head_on ? m[TN] : -INFINITY;
+      ml[(w * 16 + lr) * 2 + 1] = head_on ? lt : 0.f;
+    }
+    __syncthreads();
+    for (int item = tid; item < 16 * (D / 4); item += NW * 64) {
+      const int row = item / (D / 4);
+      const int q4 = item % (D / 4);
+      if (row >= rem_rows) continue;
+      float M = -INFINITY;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, ml[(ww * 16 + row) * 2]);
+      float Ls = 0.f;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+          const float mw = ml[(ww * 16 + row) * 2];
+          if (mw == -INFINITY) continue;
+          const float sc = __builtin_amdgcn_exp2f(mw - M);
+          Ls += sc * ml[(ww * 16 + row) * 2 + 1];
+          acc += sc * *reinterpret_cast<const f32x4*>(mo + (ww * 16 + row) * D + 4 * q4);
+        }
+      }
+      const int node = 16 * TN + row / p.g;
+      const int hd = hkv * p.g + row % p.g;
+      const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+      const float lse2 = Ls > 0.f ? M + log2f(Ls) : -INFINITY;
+      if (p.num_splits == 1) {
+        uint16_t* out = static_cast<uint16_t*>(p.out) + (int64_t)b * p.o_sb +
+                        (int64_t)node * p.o_sn + (int64_t)hd * p.o_sh + 4 * q4;
         bf16x4 v;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = static_cast<__bf16>(o[t][db][i] * inv);
-        *reinterpret_cast<bf16x4*>(out + db * 16 + 4 * lh) = v;
+        for (int i = 0; i < 4; ++i) v[i] = static_cast<__bf16>(acc[i] * inv);
+        *reinterpret_cast<bf16x4*>(out) = v;
+        if (q4 == 0 && p.lse) p.lse[((int64_t)b * p.N + node) * p.Hq + hd] = lse2 * kLn2;
+      } else {
+        const int64_t prow =
+            (((int64_t)b * p.Hkv + hkv) * p.num_splits + split) * p.R + node * p.g + row % p.g;
+        *reinterpret_cast<f32x4*>(p.ws_o + prow * D + 4 * q4) = acc * inv;
+        if (q4 == 0) p.ws_lse[prow] = lse2;
       }
-      if (lh == 0 && p.lse) p.lse[((int64_t)b * p.N + node) * p.Hq + head] = lse2 * kLn2;
-    } else {
-      const int64_t prow = (((int64_t)b * p.Hkv + hkv) * p.num_splits + split) * p.R + row;
-      float* dst = p.ws_o + prow * D;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-        *reinterpret_cast<f32x4*>(dst + db * 16 + 4 * lh) = o[t][db] * inv;
-      if (lh == 0) p.ws_lse[prow] = lse2;
     }
   }
 }
@@ -401,16 +491,19 @@ constexpr int kMfmaNST = 4;
 template <int D>
 static hipError_t launch_d(const AttnParams& p, MfmaShape sh, hipStream_t s) {
   dim3 grid(p.num_splits, p.Hkv * p.row_chunks, p.B);
-#define TV_CASE(TN, NW)                                                                   \
-  if (sh.tpw == TN && sh.nw == NW) {                                                      \
-    hipLaunchKernelGGL((tv_attn_mfma_kernel<D, kMfmaKT, kMfmaNST, TN, NW>), grid,         \
+#define TV_CASE(TN, RR, NW)                                                               \
+  if (sh.tpw == TN && sh.rr == RR && sh.nw == NW) {                                       \
+    hipLaunchKernelGGL((tv_attn_mfma_kernel<D, kMfmaKT, kMfmaNST, TN, RR, NW>), grid,     \
                        dim3(NW * 64), 0, s, p);                                           \
     return hipGetLastError();                                                             \
   }
-  TV_CASE(1, 1) TV_CASE(1, 2) TV_CASE(1, 4) TV_CASE(1, 8)
-  TV_CASE(2, 1) TV_CASE(2, 2) TV_CASE(2, 4) TV_CASE(2, 8)
-  TV_CASE(3, 1) TV_CASE(3, 2) TV_CASE(3, 4) TV_CASE(3, 8)
-  TV_CASE(4, 1) TV_CASE(4, 2) TV_CASE(4, 4) TV_CASE(4, 8)
+  TV_CASE(1, 0, 1) TV_CASE(1, 0, 2) TV_CASE(1, 0, 4) TV_CASE(1, 0, 8)
+  TV_CASE(2, 0, 1) TV_CASE(2, 0, 2) TV_CASE(2, 0, 4) TV_CASE(2, 0, 8)
+  TV_CASE(3, 0, 1) TV_CASE(3, 0, 2) TV_CASE(3, 0, 4) TV_CASE(3, 0, 8)
+  TV_CASE(4, 0, 1) TV_CASE(4, 0, 2) TV_CASE(4, 0, 4) TV_CASE(4, 0, 8)
+  TV_CASE(1, 1, 2) TV_CASE(1, 1, 4) TV_CASE(1, 1, 8)
+  TV_CASE(2, 1, 2) TV_CASE(2, 1, 4) TV_CASE(2, 1, 8)
+  TV_CASE(3, 1, 2) TV_CASE(3, 1, 4) TV_CASE(3, 1, 8)
 #undef TV_CASE
   return hipErrorInvalidConfiguration;
 }

@@ -42,9 +42,10 @@ struct AttnParams {
 };
 
 // MFMA kernel shape: `nw` waves per workgroup, one query head each; every wave owns
-// `tpw` = ceil(N/16) tiles of 16 tree nodes.
+// `tpw` tiles of 16 tree nodes.  rr = 1: the nodes past those tiles are packed across the
+// group's heads into one shared tile that the waves take turns computing.
 struct MfmaShape {
-  int tpw, nw;
+  int tpw, nw, rr;
 };
 
 hipError_t launch_attn_mfma(const AttnParams& p, int D, MfmaShape shape, hipStream_t s);
