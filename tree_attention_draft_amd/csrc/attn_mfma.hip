@@ -56,6 +56,20 @@ __device__ inline void lds_load16(const void* g, uint32_t lds) {
                :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(g) : "memory", "m0");
 }
 
+// The same copy addressed as a wave-uniform 64-bit base (SGPR pair) plus a 32-bit
+// per-lane byte offset, so advancing a whole tile costs scalar adds only.
+__device__ inline void lds_load16_s(const void* base, uint32_t voff, uint32_t lds) {
+  // readfirstlane yields a signed int: widen each half as unsigned, or a low word with
+  // bit 31 set would sign-extend over the high word
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane((uint32_t)a));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)));
+  const uint64_t sa = (static_cast<uint64_t>(hi) << 32) | static_cast<uint64_t>(lo);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(sa)
+               : "memory", "m0");
+}
+
 // Online-softmax rebasing threshold in log2 units (see the softmax step of the kernel).
 constexpr float kRebase = 8.f;
 
@@ -112,61 +126,78 @@ __device__ inline int64_t row_offset(const AttnParams& p, const RowMap& rm, int 
 // owns one 16-byte chunk: row r, LDS position lane % CH, global chunk swizzled.
 template <class C, int NW>
 struct LoadPlan {
-  int r[C::LPW];          // row within the tile
-  int coff[C::LPW];       // byte offset of the (swizzled) global chunk within the row
   bool is_v[C::LPW];      // wave-uniform
   uint32_t dst[C::LPW];   // LDS byte offset within a stage (wave-uniform)
-  const char* src0[C::LPW];  // contiguous KV: address of row r of the tile at key 0
+  uint32_t off[C::LPW];   // contiguous KV: byte offset of the chunk from the tile's row 0
 
-  __device__ LoadPlan(const AttnParams& p, const RowMap& rm, const char* kg, const char* vg,
-                      int w, int lane) {
+  // row within the tile and byte offset of the (swizzled) global chunk within the row
+  static __device__ inline void chunk_of(int ii, int w, int lane, int& r, int& coff) {
+    const int i = ii * NW + w;
+    const bool v = i >= C::LI / 2;
+    const int ik = v ? i - C::LI / 2 : i;
+    r = ik * C::RPI + lane / C::CH;
+    coff = ((lane % C::CH) ^ (v ? swz_v<C::CH>(r) : swz_k<C::CH>(r))) * 16;
+  }
+
+  __device__ LoadPlan(const AttnParams& p, int w, int lane) {
 #pragma unroll
     for (int ii = 0; ii < C::LPW; ++ii) {
       const int i = ii * NW + w;
       is_v[ii] = i >= C::LI / 2;
       const int ik = is_v[ii] ? i - C::LI / 2 : i;
-      r[ii] = ik * C::RPI + lane / C::CH;
-      const int c = (lane % C::CH) ^ (is_v[ii] ? swz_v<C::CH>(r[ii]) : swz_k<C::CH>(r[ii]));
-      coff[ii] = c * 16;
       dst[ii] = (is_v[ii] ? C::TILEB : 0) + ik * 1024;
-      src0[ii] = (is_v[ii] ? vg : kg) + (rm.head_off + (int64_t)r[ii] * p.kv_st) * 2 + coff[ii];
+      int r, coff;
+      chunk_of(ii, w, lane, r, coff);
+      off[ii] = (uint32_t)((int64_t)r * p.kv_st * 2 + coff);
     }
   }
 };
 
 // Issue the direct loads of the tile at logical key kt0 into the stage at LDS address
-// `stage`.  Full tiles of contiguous KV only add a uniform advance to precomputed
-// addresses.  Otherwise (paged KV, or the last, partial tile) rows at or past kend are
-// redirected to key kend-1 (finite data, masked out later), so every LDS slot of the stage
-// is rewritten and no read leaves [0, kend).
+// `stage`.  Full tiles of contiguous KV (`fast`: the per-lane offsets fit 32 bits) use a
+// scalar tile base plus the precomputed lane offsets.  Otherwise (paged KV, or the last,
+// partial tile) rows at or past kend are redirected to key kend-1 (finite data, masked
+// out later), so every LDS slot of the stage is rewritten and no read leaves [0, kend).
 template <class C, int NW, int KT>
 __device__ inline void issue_tile(const AttnParams& p, const RowMap& rm,
                                   const LoadPlan<C, NW>& lp, const char* kg, const char* vg,
-                                  uint32_t stage, int kt0, int kend) {
-  if (!p.paged && kt0 + KT <= kend) {
-    const int64_t adv = (int64_t)kt0 * p.kv_st * 2;
+                                  uint32_t stage, int kt0, int kend, bool fast, int w,
+                                  int lane) {
+  if (fast && kt0 + KT <= kend) {
+    const int64_t row0 = (rm.head_off + (int64_t)kt0 * p.kv_st) * 2;
+    const char* kb = kg + row0;
+    const char* vb = vg + row0;
 #pragma unroll
-    for (int ii = 0; ii < C::LPW; ++ii) lds_load16(lp.src0[ii] + adv, stage + lp.dst[ii]);
+    for (int ii = 0; ii < C::LPW; ++ii)
+      lds_load16_s(lp.is_v[ii] ? vb : kb, lp.off[ii], stage + lp.dst[ii]);
     return;
   }
 #pragma unroll
   for (int ii = 0; ii < C::LPW; ++ii) {
-    const int t = min(kt0 + lp.r[ii], kend - 1);
-    const char* src = (lp.is_v[ii] ? vg : kg) + row_offset(p, rm, t) * 2 + lp.coff[ii];
+    int r, coff;
+    LoadPlan<C, NW>::chunk_of(ii, w, lane, r, coff);
+    const int t = min(kt0 + r, kend - 1);
+    const char* src = (lp.is_v[ii] ? vg : kg) + row_offset(p, rm, t) * 2 + coff;
     lds_load16(src, stage + lp.dst[ii]);
   }
 }
 
 // Online softmax of one 16-row x KT-key score tile held transposed (lane: 4 keys of one
 // row per 16-key block), with lazy rebasing: a row keeps its reference max m until one of
-// its scores exceeds it by more than kRebase (log2 units).  Each lane tests only its own
-// scores; the row max over lanes and the O/l rescale run only when some lane trips the
-// test, which after the first tile is rare.  Exponents stay <= kRebase, so P <= 2^kRebase
-// (no overflow in fp32 or bf16) and the final division by l cancels the reference.
-// `allow` (masked tiles only) holds this lane's allowed-key bits: bit 16*kb + i.
-template <int KB, int KS, int DB>
-__device__ inline void softmax_tile(f32x4 (&sacc)[KB], float& m, float& l, f32x4 (&o)[DB],
-                                    bf16x8 (&pk)[KS], float c, bool masked, uint64_t allow) {
+// its scores exceeds it by more than kRebase (log2 units).  Per-row state kept per lane:
+//   m    reference max in scaled log2 units (-inf before the first finite score)
+//   nm   -m, or 0 while m is -inf: the addend of the exponent
+//   thr  (m + kRebase) / c: the rebase test in raw score units (c > 0)
+//   l    this lane's share of the row sum, in units of 2^m
+// Each lane tests only its own raw scores against thr; the row max over lanes and the
+// O/l rescale run only when some lane trips the test, which after the first tile is
+// rare.  Exponents stay <= kRebase, so P <= 2^kRebase (no overflow in fp32 or bf16) and
+// the final division by l cancels the reference.
+
+// Masks the tile (masked tiles only) and returns this lane's raw max.  `allow` holds this
+// lane's allowed-key bits: bit 16*kb + i.
+template <int KB>
+__device__ inline float mask_and_max(f32x4 (&sacc)[KB], bool masked, uint64_t allow) {
   if (masked) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -174,36 +205,55 @@ __device__ inline void softmax_tile(f32x4 (&sacc)[KB], float& m, float& l, f32x4
       for (int i = 0; i < 4; ++i)
         sacc[kb][i] = ((allow >> (16 * kb + i)) & 1ull) ? sacc[kb][i] : -INFINITY;
   }
-  float mx = -INFINITY;
+  float mx = sacc[0][0];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[kb][i]);
-  mx *= c;
-  if (__any(mx > m + kRebase)) {  // wave-uniform branch
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
+    for (int i = (kb == 0 ? 1 : 0); i < 4; ++i) mx = fmaxf(mx, sacc[kb][i]);
+  return mx;
+}
+
+// Rare path: move the row's reference to its current max and rescale what was summed.
+template <int DB>
+__device__ inline void rebase_row(float mx_raw, float c, float& m, float& nm, float& thr,
+                                  float& l, f32x4 (&o)[DB]) {
+  float mx = mx_raw * c;
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(m, mx);
+  if (m_new != -INFINITY) {
     const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 when m was -inf
-    if (m_new != -INFINITY) {
-      l *= alpha;
+    l *= alpha;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
-      m = m_new;
+    for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    m = m_new;
+    nm = -m_new;
+    thr = (m_new + kRebase) / c;
+  }
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// P = 2^(c*s - m) packed to bf16 as the B operand of P.V; the row sum accumulates the
+// same rounded values (dot with (1, 1)), so numerator and denominator use equal weights.
+template <int KB, int KS>
+__device__ inline void exp_pack(const f32x4 (&sacc)[KB], float c, float nm, float& l,
+                                bf16x8 (&pk)[KS]) {
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      pk[kb >> 1][(kb & 1) * 4 + i] =
+          static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, nm)));
+  const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const bf16x2 pair = {pk[ks][2 * h], pk[ks][2 * h + 1]};
+      l = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, l, false);
     }
   }
-  const float m_use = (m == -INFINITY) ? 0.f : m;
-  float rs = 0.f;
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, -m_use));
-      rs += e;
-      pk[kb >> 1][(kb & 1) * 4 + i] = static_cast<__bf16>(e);
-    }
-  }
-  l += rs;
 }
 
 // Final store of one row: normalised output and natural-log LSE, or the split partial.
@@ -231,6 +281,20 @@ __device__ inline void store_row_block(const AttnParams& p, int b, int hkv, int 
     for (int db = 0; db < D / 16; ++db)
       *reinterpret_cast<f32x4*>(dst + db * 16 + 4 * lh) = o[db] * inv;
     if (lh == 0) p.ws_lse[prow] = lse2;
+  }
+}
+
+// Waits until at most n (0 <= n <= MAXN) tiles' worth of this wave's direct loads remain.
+template <int LPW, int MAXN>
+__device__ inline void wait_tiles(int n) {
+  if constexpr (MAXN > 0) {
+    if (n >= MAXN) {
+      wait_vmcnt<MAXN * LPW>();
+      return;
+    }
+    wait_tiles<LPW, MAXN - 1>(n);
+  } else {
+    wait_vmcnt<0>();
   }
 }
 
@@ -327,36 +391,31 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
   wait_vmcnt<0>();
   __syncthreads();  // mask_s and pt_s visible
 
-  // ---- start the first NST-1 tiles streaming ----
-  const LoadPlan<C, NW> lp(p, rm, kg, vg, w, lane);
+  // ---- start the first two windows streaming ----
+  const LoadPlan<C, NW> lp(p, w, lane);
+  const bool fast = !p.paged && (int64_t)(KT - 1) * p.kv_st * 2 + 2 * D <= INT32_MAX;
 #pragma unroll
-  for (int s = 0; s < NST - 1; ++s)
+  for (int s = 0; s < NST; ++s)
     if (s < ntiles)
-      issue_tile<C, NW, KT>(p, rm, lp, kg, vg, sbase + s * C::STAGEB, kbeg + s * KT, kend);
+      issue_tile<C, NW, KT>(p, rm, lp, kg, vg, sbase + s * C::STAGEB, kbeg + s * KT, kend, fast,
+                            w, lane);
 
   f32x4 o[TT][DB];
-  float m[TT], l[TT];
+  float m[TT], l[TT], nm[TT], thr[TT];
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
     m[t] = -INFINITY;
+    thr[t] = -INFINITY;
+    nm[t] = 0.f;
     l[t] = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[t][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float c = p.scale_log2;
 
-  for (int it = 0; it < ntiles; ++it) {
+  // One key tile: S^T = K Q^T, mask, online softmax, O^T += V^T P^T.
+  auto tile = [&](int it, bool do_rem) {
     const int kt0 = kbeg + it * KT;
-    // my loads of tile `it` are complete once at most (tiles issued after it) x LPW remain
-    if (it + NST - 2 < ntiles) wait_vmcnt<(NST - 2) * C::LPW>();
-    else wait_vmcnt<0>();
-    __syncthreads();  // tile `it` visible to all waves; the stage of tile it-1 is free
-    if (it + NST - 1 < ntiles)
-      issue_tile<C, NW, KT>(p, rm, lp, kg, vg, sbase + ((it + NST - 1) % NST) * C::STAGEB,
-                            kt0 + (NST - 1) * KT, kend);
-    if (!head_on) continue;  // surplus wave of a group smaller than NW: loads only
-    const bool do_rem = RR && (it % NW) == w;  // wave-uniform
-
     const char* ks = smem + (it % NST) * C::STAGEB;
     const char* vs = ks + C::TILEB;
 
@@ -381,14 +440,31 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
       }
     }
 
-    // ---- tree-tail mask, online softmax, P packing ----
+    // ---- tree-tail mask, lazy rebase test ----
     const bool masked = kt0 + KT > L;
-    bf16x8 pk[TT][KS];
+    float mx[TT];
+    bool trip = false;
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
       if (t >= TN && !do_rem) continue;
       const uint64_t allow = masked ? tile_allowed(mask_s[node_of[t]], kt0, L) >> (4 * lh) : 0ull;
-      softmax_tile<KB, KS, DB>(sacc[t], m[t], l[t], o[t], pk[t], c, masked, allow);
+      mx[t] = mask_and_max<KB>(sacc[t], masked, allow);
+      trip |= mx[t] > thr[t];
+    }
+    if (__any(trip)) {  // wave-uniform, rare after the first tile
+#pragma unroll
+      for (int t = 0; t < TT; ++t) {
+        if (t >= TN && !do_rem) continue;
+        if (__any(mx[t] > thr[t])) rebase_row<DB>(mx[t], c, m[t], nm[t], thr[t], l[t], o[t]);
+      }
+    }
+
+    // ---- P, row sums ----
+    bf16x8 pk[TT][KS];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      if (t >= TN && !do_rem) continue;
+      exp_pack<KB, KS>(sacc[t], c, nm[t], l[t], pk[t]);
     }
 
     // ---- O^T += V^T P^T, V^T read transposed from V's row-major tile ----
@@ -413,6 +489,36 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
           o[t][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pk[t][kss], o[t][db], 0, 0, 0);
         }
       }
+    }
+  };
+
+  // Tiles go in windows of WIN = NST/2: one barrier per window publishes its WIN tiles and
+  // frees the stages of the previous window, whose loads for the next window then stream
+  // while this one is computed.  The shared remainder tile of key tile `it` is computed by
+  // wave it % NW, so within a window the extra work lands on WIN different waves.
+  constexpr int WIN = NST / 2;
+  for (int it = 0; it < ntiles; it += WIN) {
+    if (it == 0) {
+      // the prologue issued tiles 0 .. min(NST, ntiles)-1; tiles of window 1 may remain
+      wait_tiles<C::LPW, WIN>(min(ntiles, NST) - min(ntiles, WIN));
+    } else {
+      wait_vmcnt<0>();  // this window's tiles were the last ones issued
+    }
+    __syncthreads();  // window visible to all waves; the previous window's stages are free
+    if (it > 0) {
+#pragma unroll
+      for (int s = 0; s < WIN; ++s) {
+        const int tn = it + WIN + s;
+        if (tn < ntiles)
+          issue_tile<C, NW, KT>(p, rm, lp, kg, vg, sbase + (tn % NST) * C::STAGEB,
+                                kbeg + tn * KT, kend, fast, w, lane);
+      }
+    }
+    if (!head_on) continue;  // surplus wave of a group smaller than NW: loads only
+#pragma unroll
+    for (int s = 0; s < WIN; ++s) {
+      const int tt = it + s;
+      if (tt < ntiles) tile(tt, RR && (tt % NW) == w);
     }
   }
 
