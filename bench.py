@@ -60,7 +60,18 @@ def algorithmic_flops(prefix_lens, depths, Hq, D):
     return total
 
 
-def cpu_baseline(host, trees_parent, prefix_lens, N, budget_s):
+def request_kv(host, b, T, page_size):
+    """fp64 K and V of request b over its first T tokens (gathered from pages if paged)."""
+    from oracle import attn as oattn
+    if page_size:
+        k = oattn.gather_paged(host["k"], host["page_table"][b], page_size, T)
+        v = oattn.gather_paged(host["v"], host["page_table"][b], page_size, T)
+    else:
+        k, v = host["k"][b, :T], host["v"][b, :T]
+    return oattn.bf16_bits_to_f64(k), oattn.bf16_bits_to_f64(v)
+
+
+def cpu_baseline(host, trees_parent, prefix_lens, N, budget_s, page_size=0):
     """Time the fp64 oracle (as it stands) on whole requests until the budget is spent."""
     import numpy as np
     from oracle import attn as oattn
@@ -78,8 +89,7 @@ def cpu_baseline(host, trees_parent, prefix_lens, N, budget_s):
         b = done % B
         T = int(prefix_lens[b]) + N
         q = oattn.bf16_bits_to_f64(host["q"][b])
-        k = oattn.bf16_bits_to_f64(host["k"][b, :T])
-        v = oattn.bf16_bits_to_f64(host["v"][b, :T])
+        k, v = request_kv(host, b, T, page_size)
         oattn.tree_attention_request(q, k, v, trees_parent[b], int(prefix_lens[b]))
         done += 1
     el = time.perf_counter() - t0
@@ -87,6 +97,18 @@ def cpu_baseline(host, trees_parent, prefix_lens, N, budget_s):
             "kind": "oracle",
             "sample": f"{done} whole requests ({done / B:.1f} passes over the {B}-request "
                       f"batch; all nodes and heads), fp64 numpy oracle, {el:.1f} s"}
+
+
+def describe(name, spec, B, N, Lmax, page):
+    if name == "b64_l4096_n33" and B == 64:
+        return ("tree-verify attention: B=64 requests, prefix L=4096, N=33-node random draft "
+                "trees (depth<=8), GQA 32q/8kv, D=128, bf16, contiguous KV")
+    L = spec["L"]
+    lstr = f"ragged L~U[{L[0]},{L[1]}]" if isinstance(L, tuple) else f"prefix L={Lmax}"
+    tree = spec["tree"] if spec["tree"] != "random" else f"random trees (depth<={spec['cap']})"
+    kv = f"paged KV (page {page})" if page else "contiguous KV"
+    return (f"tree-verify attention ({name}): B={B} requests, {lstr}, N={N}-node {tree}, "
+            f"GQA {spec['Hq']}q/{spec['Hkv']}kv, D={spec['D']}, bf16, {kv}")
 
 
 def main():
@@ -98,6 +120,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (counter scaling reference)")
+    ap.add_argument("--workload", default="b64_l4096_n33",
+                    help="bf16 workload name (default: the B=64, L=4096, N=33 batch)")
+    ap.add_argument("--batch", type=int, default=0, help="override the workload's batch")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -115,19 +140,28 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    spec = workloads.WORKLOADS["b64_l4096_n33"]
-    B, N, Hq, Hkv, D = spec["B"], spec["N"], spec["Hq"], spec["Hkv"], spec["D"]
+    spec = dict(workloads.WORKLOADS[args.workload])
+    if spec["dtype"] != "bf16":
+        sys.exit(f"bench.py: {args.workload} is not a bf16 workload")
+    if args.batch:
+        spec["B"] = args.batch
+    B, Hq, Hkv, D = spec["B"], spec["Hq"], spec["Hkv"], spec["D"]
     trees, _ = workloads.trees_for(spec)
+    N = spec.get("N", 1 + max((len(t) for t in trees), default=0))  # paths exclude the root
     L = workloads.prefix_lengths(spec)
     Lmax = int(L.max())
-    print(f"[bench] generating inputs B={B} L={Lmax} N={N} Hq={Hq} Hkv={Hkv} D={D}",
-          file=sys.stderr, flush=True)
-    host = workloads.build_batch(1000 + spec["k"], L, N, Hq, Hkv, D, "bf16")
+    page = int(spec.get("paged", 0))
+    print(f"[bench] generating inputs {args.workload} B={B} L<={Lmax} N={N} Hq={Hq} "
+          f"Hkv={Hkv} D={D} page={page}", file=sys.stderr, flush=True)
+    host = workloads.build_batch(1000 + spec["k"], L, N, Hq, Hkv, D, "bf16",
+                                 k_scale=spec.get("k_scale", False), page_size=page,
+                                 page_seed=3000 + spec["k"])
 
     def up(a):
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
 
     q, k, v = up(host["q"]), up(host["k"]), up(host["v"])
+    pt_dev = torch.from_numpy(host["page_table"]).to(dev) if page else None
     prefix_dev = torch.from_numpy(L).to(dev)
     packed = tv.PackedTrees(trees)
     pin = [torch.empty((B, N), dtype=torch.int32, pin_memory=True) for _ in range(2)]
@@ -141,7 +175,8 @@ def main():
     d_pos = torch.empty((B, N), dtype=torch.int32, device=dev)
     out = torch.empty_like(q)
     lse = torch.empty((B, N, Hq), dtype=torch.float32, device=dev)
-    ws_bytes = tv.tree_verify_attn_workspace_size(q, k, v, parent_dev[0], prefix_dev, Lmax)
+    ws_bytes = tv.tree_verify_attn_workspace_size(q, k, v, parent_dev[0], prefix_dev, Lmax,
+                                                  page_table=pt_dev, page_size=page)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     copy_done = [torch.cuda.Event() for _ in range(2)]
     for e in copy_done:
@@ -160,8 +195,8 @@ def main():
         tv.tree_meta_from_parent(parent_dev[s], prefix_dev, depth=d_depth, bitmask=d_mask,
                                  pos=d_pos)
         ev_a[i].record()
-        tv.tree_verify_attn(q, k, v, parent_dev[s], prefix_dev, Lmax, out=out, lse=lse,
-                            workspace=ws)
+        tv.tree_verify_attn(q, k, v, parent_dev[s], prefix_dev, Lmax, page_table=pt_dev,
+                            page_size=page, out=out, lse=lse, workspace=ws)
         ev_b[i].record()
 
     print("[bench] warmup", file=sys.stderr, flush=True)
@@ -187,9 +222,9 @@ def main():
     sample = [0, B - 1]
     for b in sample:
         T = int(L[b]) + N
-        o, l = oattn.tree_attention_request(
-            oattn.bf16_bits_to_f64(host["q"][b]), oattn.bf16_bits_to_f64(host["k"][b, :T]),
-            oattn.bf16_bits_to_f64(host["v"][b, :T]), ref_parent[b], int(L[b]))
+        kb, vb = request_kv(host, b, T, page)
+        o, l = oattn.tree_attention_request(oattn.bf16_bits_to_f64(host["q"][b]), kb, vb,
+                                            ref_parent[b], int(L[b]))
         worst = max(worst, float(np.abs(out_h[b] - o).max()), float(np.abs(lse_h[b] - l).max()))
     parity_ok = worst <= 2e-2
 
@@ -200,12 +235,12 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    alg_bytes = algorithmic_bytes(L, N, Hq, Hkv, D, 2)
+    alg_bytes = algorithmic_bytes(L, N, Hq, Hkv, D, 2, paged_page=page)
     depths = [ometa.meta_from_parent(p, 0)["depth"] for p in ref_parent]
     flops = algorithmic_flops(L, depths, Hq, D)
     achieved = alg_bytes / kern_avg_s / 1e9
     traffic = None
-    if os.path.exists(COUNTERS):
+    if args.workload == "b64_l4096_n33" and not args.batch and os.path.exists(COUNTERS):
         with open(COUNTERS) as fh:
             c = json.load(fh)
         if c.get("kernel_source_hash") == kernel_source_hash():
@@ -225,11 +260,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "tree-verify attention: B=64 requests, prefix L=4096, N=33-node "
-                        "random draft trees (depth<=8), GQA 32q/8kv, D=128, bf16, "
-                        "contiguous KV",
+            "workload": describe(args.workload, spec, B, N, Lmax, page),
             "B": B, "L": Lmax, "N": N, "Hq": Hq, "Hkv": Hkv, "D": D,
-            "kv_layout": "contiguous", "splits": "auto",
+            "kv_layout": f"paged{page}" if page else "contiguous", "splits": "auto",
             "workspace_bytes": ws_bytes,
         },
         "roofline": {
@@ -250,7 +283,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(host, ref_parent, L, N, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(host, ref_parent, L, N, args.cpu_seconds, page)
     print(json.dumps(result), flush=True)
     if not parity_ok:
         sys.exit(1)

@@ -94,12 +94,24 @@ def test_llama8b_shape_full(tree):
 
 
 # ------------------------------------------------------------------ shapes & paths ----
-@pytest.mark.parametrize("N", [1, 2, 5, 10, 16, 17, 33, 63, 64])
+@pytest.mark.parametrize("N", [1, 2, 5, 10, 16, 17, 33, 49, 50, 63, 64])
 def test_node_count_sweep(N):
     paths, _ = random_trees(500 + N, 2, N, 8)
     c = Case(f"nodes{N}", [300, 77], trees=paths, seed=1100 + N)
     out, lse = c.run()
     c.check(out, lse)
+
+
+@pytest.mark.parametrize("N", [64])
+@pytest.mark.parametrize("hq,hkv", [(64, 8), (16, 8)])
+def test_node_chunks(N, hq, hkv):
+    # 64 nodes = four 16-node tiles per head: split over two workgroups per kv head
+    paths, _ = random_trees(700 + hq, 3, N, 10)
+    c = Case(f"nodechunks{hq}_{hkv}", [1000, 33, 0], trees=paths, Hq=hq, Hkv=hkv,
+             seed=1300 + hq)
+    for splits in (0, 3):
+        out, lse = c.run(num_splits=splits)
+        c.check(out, lse)
 
 
 @pytest.mark.parametrize("D", [64, 128])

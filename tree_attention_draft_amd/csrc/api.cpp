@@ -21,6 +21,8 @@ struct Plan {
   bool mfma = false;
   MfmaShape shape{1, 1};
   int row_chunks = 1;
+  int head_chunks = 1;
+  int node_chunks = 1;
   int rows_per_wg = 16;
   int splits = 1;
   int chunk = kKeysPerTile;
@@ -61,9 +63,12 @@ MfmaShape pick_mfma_shape(int N, int g, int* head_chunks) {
   while (nw < g && nw < 8) nw *= 2;
   *head_chunks = (g + nw - 1) / nw;
   const int full = N / 16, rem = N % 16;
-  if (nw == g && g >= 2 && full >= 1 && full <= 3 && rem > 0 && rem * g <= 16)
-    return MfmaShape{full, nw, 1};
-  return MfmaShape{(N + 15) / 16, nw, 0};
+  if (nw == g && g >= 2 && full >= 1 && full <= 2 && rem > 0 && rem * g <= 16)
+    return MfmaShape{full, nw, 1, 1};
+  // a wave holds at most three 16-node tiles of state; more are split over node chunks
+  const int tiles = (N + 15) / 16;
+  const int nc = (tiles + 2) / 3;
+  return MfmaShape{(tiles + nc - 1) / nc, nw, 0, nc};
 }
 
 tv_status check_args(const tv_attn_args* a, bool pointers) {
@@ -118,11 +123,15 @@ tv_status make_plan(const tv_attn_args* a, Plan* pl) {
   const bool bf16 = a->dtype == TV_BF16;
   pl->mfma = a->path == TV_PATH_MFMA || (a->path == TV_PATH_AUTO && bf16 && R >= 16);
   if (pl->mfma) {
-    pl->shape = pick_mfma_shape(a->N, g, &pl->row_chunks);
+    pl->shape = pick_mfma_shape(a->N, g, &pl->head_chunks);
+    pl->node_chunks = pl->shape.nc;
+    pl->row_chunks = pl->head_chunks * pl->node_chunks;
     pl->rows_per_wg = pl->shape.nw * a->N;
   } else {
     pl->rows_per_wg = kValuRowsPerWg;
     pl->row_chunks = (R + kValuRowsPerWg - 1) / kValuRowsPerWg;
+    pl->head_chunks = pl->row_chunks;
+    pl->node_chunks = 1;
   }
   if ((int64_t)a->Hkv * pl->row_chunks > 65535)
     return fail(TV_ERR_UNSUPPORTED, "Hkv * row chunks > 65535");
@@ -194,6 +203,8 @@ AttnParams make_params(const tv_attn_args* a, const Plan& pl) {
   p.num_splits = pl.splits;
   p.chunk = pl.chunk;
   p.row_chunks = pl.row_chunks;
+  p.head_chunks = pl.head_chunks;
+  p.node_chunks = pl.node_chunks;
   p.rows_per_wg = pl.rows_per_wg;
   const float scale = a->sm_scale > 0.f ? a->sm_scale : 1.0f / std::sqrt((float)a->D);
   p.scale_log2 = scale * 1.4426950408889634f;

@@ -321,7 +321,8 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
   const int lh = lane >> 4;
   const int split = blockIdx.x;
   const int hkv = blockIdx.y % p.Hkv;
-  const int hc = blockIdx.y / p.Hkv;
+  const int hc = (blockIdx.y / p.Hkv) % p.head_chunks;
+  const int t0 = (blockIdx.y / p.Hkv / p.head_chunks) * TN;  // first 16-node tile of this wg
   const int b = blockIdx.z;
   const int L = clamped_prefix(p, b);
   const int Ttot = L + p.N;
@@ -348,8 +349,8 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
   for (int t = 0; t < TT; ++t) {
     int node, hd;
     bool valid;
-    if (t < TN) {  // full tiles: head-major, every one holds at least one real node
-      node = t * 16 + lr;
+    if (t < TN) {  // full tiles: head-major (rows past N are padding)
+      node = (t0 + t) * 16 + lr;
       hd = head;
       valid = head_on && node < p.N;
     } else {       // shared remainder tile: node-major across the group's heads
@@ -529,7 +530,7 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
       float lt = l[t];
       lt += __shfl_xor(lt, 16);
       lt += __shfl_xor(lt, 32);
-      const int node = t * 16 + lr;
+      const int node = (t0 + t) * 16 + lr;
       if (node < p.N)
         store_row_block<D>(p, b, hkv, split, node, head, node * p.g + j, lh, o[t], m[t], lt);
     }
@@ -606,10 +607,8 @@ static hipError_t launch_d(const AttnParams& p, MfmaShape sh, hipStream_t s) {
   TV_CASE(1, 0, 1) TV_CASE(1, 0, 2) TV_CASE(1, 0, 4) TV_CASE(1, 0, 8)
   TV_CASE(2, 0, 1) TV_CASE(2, 0, 2) TV_CASE(2, 0, 4) TV_CASE(2, 0, 8)
   TV_CASE(3, 0, 1) TV_CASE(3, 0, 2) TV_CASE(3, 0, 4) TV_CASE(3, 0, 8)
-  TV_CASE(4, 0, 1) TV_CASE(4, 0, 2) TV_CASE(4, 0, 4) TV_CASE(4, 0, 8)
   TV_CASE(1, 1, 2) TV_CASE(1, 1, 4) TV_CASE(1, 1, 8)
   TV_CASE(2, 1, 2) TV_CASE(2, 1, 4) TV_CASE(2, 1, 8)
-  TV_CASE(3, 1, 2) TV_CASE(3, 1, 4) TV_CASE(3, 1, 8)
 #undef TV_CASE
   return hipErrorInvalidConfiguration;
 }

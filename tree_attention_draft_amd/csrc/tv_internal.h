@@ -36,16 +36,21 @@ struct AttnParams {
   int32_t B, N, Hq, Hkv, g, R;
   int32_t num_splits;  // S
   int32_t chunk;       // keys per split, a multiple of kKeysPerTile
-  int32_t row_chunks;  // workgroups along the packed-row (MFMA: query-head) dimension
+  int32_t row_chunks;  // workgroups along the packed-row dimension (MFMA: head chunks x
+                       // node chunks, head chunk fastest)
+  int32_t head_chunks; // MFMA: workgroups splitting the group's query heads
+  int32_t node_chunks; // MFMA: workgroups splitting each head's 16-node tiles
   int32_t rows_per_wg; // packed rows one workgroup covers
   float scale_log2;    // sm_scale * log2(e)
 };
 
 // MFMA kernel shape: `nw` waves per workgroup, one query head each; every wave owns
 // `tpw` tiles of 16 tree nodes.  rr = 1: the nodes past those tiles are packed across the
-// group's heads into one shared tile that the waves take turns computing.
+// group's heads into one shared tile that the waves take turns computing.  nc > 1: a
+// head's tiles are split over nc workgroups (a wave keeps at most three tiles of state in
+// registers), each streaming the same keys.
 struct MfmaShape {
-  int tpw, nw, rr;
+  int tpw, nw, rr, nc;
 };
 
 hipError_t launch_attn_mfma(const AttnParams& p, int D, MfmaShape shape, hipStream_t s);
