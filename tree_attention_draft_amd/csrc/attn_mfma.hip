@@ -420,24 +420,44 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
     const char* ks = smem + (it % NST) * C::STAGEB;
     const char* vs = ks + C::TILEB;
 
-    // ---- S^T = K Q^T ----
+    // ---- S^T = K Q^T.  Full tiles: step s of key block kb+1 is read right after the last
+    // MFMA that uses step s of block kb, so the reads overlap matrix work without extra
+    // registers.  The shared tile (this wave's turn only) re-reads its K operand after. ----
     f32x4 sacc[TT][KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const int r = kb * 16 + lr;
+    {
+      auto read_k = [&](int kb, int s) {
+        const int r = kb * 16 + lr;
+        return *reinterpret_cast<const bf16x8*>(ks + r * C::ROWB +
+                                                (((4 * s + lh) ^ swz_k<C::CH>(r)) << 4));
+      };
       bf16x8 ka[DS];
 #pragma unroll
-      for (int s = 0; s < DS; ++s)
-        ka[s] = *reinterpret_cast<const bf16x8*>(ks + r * C::ROWB +
-                                                 (((4 * s + lh) ^ swz_k<C::CH>(r)) << 4));
+      for (int s = 0; s < DS; ++s) ka[s] = read_k(0, s);
 #pragma unroll
-      for (int t = 0; t < TT; ++t) {
-        if (t >= TN && !do_rem) continue;
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < KB; ++kb) {
+        f32x4 acc[TN];
 #pragma unroll
-        for (int s = 0; s < DS; ++s)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s], qreg[t][s], acc, 0, 0, 0);
-        sacc[t][kb] = acc;
+        for (int t = 0; t < TN; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < DS; ++s) {
+#pragma unroll
+          for (int t = 0; t < TN; ++t)
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s], qreg[t][s], acc[t], 0, 0, 0);
+          if (kb + 1 < KB) ka[s] = read_k(kb + 1, s);
+        }
+#pragma unroll
+        for (int t = 0; t < TN; ++t) sacc[t][kb] = acc[t];
+      }
+      if (RR && do_rem) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < DS; ++s)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_k(kb, s), qreg[TT - 1][s], acc, 0,
+                                                          0, 0);
+          sacc[TT - 1][kb] = acc;
+        }
       }
     }
 
@@ -468,27 +488,35 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
       exp_pack<KB, KS>(sacc[t], c, nm[t], l[t], pk[t]);
     }
 
-    // ---- O^T += V^T P^T, V^T read transposed from V's row-major tile ----
+    // ---- O^T += V^T P^T, V^T read transposed from V's row-major tile.  The operand of
+    // feature block db+1 is read before the MFMAs of block db, so the LDS latency of every
+    // block but the first overlaps matrix work. ----
     const int q4 = lr & 3;                       // which 4-feature group this lane addresses
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    auto read_v = [&](int db, int kss) {
       const int chunk = 2 * db + (q4 >> 1);      // 16-byte chunk of features 16db + 4q4
       const int half = (q4 & 1) << 3;            // byte offset inside the chunk
+      const int r0 = 32 * kss + 4 * lh + (lr >> 2);
+      const int r1 = r0 + 16;
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (TV_LDS v4i16*)(vs + r0 * C::ROWB + ((chunk ^ swz_v<C::CH>(r0)) << 4) + half));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (TV_LDS v4i16*)(vs + r1 * C::ROWB + ((chunk ^ swz_v<C::CH>(r1)) << 4) + half));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    constexpr int NV = DB * KS;                  // V operands per tile, db-major
+    constexpr int PF = 1;                        // operands in flight ahead of the MFMAs
+    bf16x8 va[PF + 1];
 #pragma unroll
-      for (int kss = 0; kss < KS; ++kss) {
-        const int r0 = 32 * kss + 4 * lh + (lr >> 2);
-        const int r1 = r0 + 16;
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (TV_LDS v4i16*)(vs + r0 * C::ROWB + ((chunk ^ swz_v<C::CH>(r0)) << 4) + half));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (TV_LDS v4i16*)(vs + r1 * C::ROWB + ((chunk ^ swz_v<C::CH>(r1)) << 4) + half));
-        const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        const bf16x8 va = __builtin_bit_cast(bf16x8, both);
+    for (int iv = 0; iv < PF && iv < NV; ++iv) va[iv] = read_v(iv / KS, iv % KS);
 #pragma unroll
-        for (int t = 0; t < TT; ++t) {
-          if (t >= TN && !do_rem) continue;
-          o[t][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pk[t][kss], o[t][db], 0, 0, 0);
-        }
+    for (int iv = 0; iv < NV; ++iv) {
+      const int db = iv / KS, kss = iv % KS;
+      if (iv + PF < NV) va[(iv + PF) % (PF + 1)] = read_v((iv + PF) / KS, (iv + PF) % KS);
+#pragma unroll
+      for (int t = 0; t < TT; ++t) {
+        if (t >= TN && !do_rem) continue;
+        o[t][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[iv % (PF + 1)], pk[t][kss],
+                                                           o[t][db], 0, 0, 0);
       }
     }
   };
