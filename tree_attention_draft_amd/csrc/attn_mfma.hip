@@ -7,16 +7,20 @@
 // and turned into one 64-bit "allowed" word per row per key tile; tiles that hold only
 // prefix keys carry no mask at all.
 //
-// Work decomposition.  One workgroup = (key split, kv head x head chunk, request) with NW
-// waves; wave w owns query head j = chunk*NW + w of the group and all its TN 16-node tiles,
-// so every wave does the same amount of work.  Each 64-key tile of K and V is read from
-// HBM once per workgroup and reused by every head and node of the group.
+// Work decomposition.  One workgroup = (key split, kv head x head chunk x node chunk,
+// request) with NW waves; wave w owns query head j = chunk*NW + w of the group and TN of
+// its 16-node tiles (all of them unless long trees are split over node chunks), so every
+// wave does the same amount of work; the nodes past the last full tile of all heads can
+// share one tile that the waves take turns computing (RR, below).  Each 32-key tile of K
+// and V is read from HBM once per workgroup and reused by every head and node of it.
 //
 // Memory pipeline.  K and V tiles are copied global -> LDS by direct loads
-// (global_load_lds, 16 bytes per lane) into an NST-stage ring: no registers are tied up in
-// flight, and tile t+NST-1 is loading while tile t is computed.  One barrier per tile both
-// publishes tile t and frees the stage of tile t-1.  LDS rows are XOR-swizzled per 16-byte
-// chunk (K by row, V by row pairs; see swz_k / swz_v) so operand reads are conflict-free.
+// (global_load_lds, 16 bytes per lane) into an NST-stage ring holding two windows of NST/2
+// tiles: no registers are tied up in flight.  One barrier per window publishes its tiles
+// and frees the previous window's stages, into which the next window's loads are issued
+// right away, so they stream while this window is computed.  LDS rows are XOR-swizzled
+// per 16-byte chunk (K by row, V by row pairs; see swz_k / swz_v) so operand reads are
+// conflict-free.
 //
 // Matrix-core layout (v_mfma_f32_16x16x32_bf16; lane l, lr = l % 16, lh = l / 16):
 //   A operand: row lr, k = 8*lh .. 8*lh+7;  B operand: column lr, same k;
