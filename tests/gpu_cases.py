@@ -38,6 +38,7 @@ class Case:
         self.N = len(self.parent_gpu[0])
         assert all(len(p) == self.N for p in self.parent_gpu)
         self.page_size = page_size
+        self.sm_scale = None  # the oracle's default (1/sqrt(D)) unless a run sets one
         say(name, f"B={self.B} N={self.N} Hq={Hq} Hkv={Hkv} D={D} {dtype} "
             f"L=[{self.L.min() if self.B else 0},{self.L.max() if self.B else 0}] "
             f"paged={page_size} seed={seed}")
@@ -71,6 +72,8 @@ class Case:
             kw.setdefault("page_table", d["page_table"])
             kw.setdefault("page_size", self.page_size)
         parent = kw.pop("parent", d["parent"])
+        if kw.get("sm_scale"):
+            self.sm_scale = float(kw["sm_scale"])
         say(self.name, "tree_verify_attn", {k: v for k, v in kw.items()
                                             if k in ("num_splits", "path", "max_prefix_len")})
         out, lse = tv.tree_verify_attn(d["q"], d["k"], d["v"], parent, d["prefix_len"], **kw)
@@ -97,7 +100,8 @@ class Case:
 
     def oracle(self, b):
         q, k, v = self.request_inputs(b)
-        return oattn.tree_attention_request(q, k, v, self.parent_oracle[b], int(self.L[b]))
+        return oattn.tree_attention_request(q, k, v, self.parent_oracle[b], int(self.L[b]),
+                                            sm_scale=self.sm_scale)
 
     def check(self, out, lse, requests=None, tol=None):
         """Max-abs error of the given outputs vs the oracle over ``requests`` (all by

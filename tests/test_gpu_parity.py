@@ -102,6 +102,26 @@ def test_node_count_sweep(N):
     c.check(out, lse)
 
 
+@pytest.mark.parametrize("hq,hkv", [(64, 4), (16, 8), (8, 1)])
+def test_group_sizes_n33(hq, hkv):
+    # g = 16 (two head chunks of 8 waves), g = 2, g = 8 with one kv head
+    paths, _ = random_trees(800 + hq, 2, 33, 8)
+    c = Case(f"groups{hq}_{hkv}", [515, 64], trees=paths, Hq=hq, Hkv=hkv, seed=1400 + hq)
+    out, lse = c.run()
+    c.check(out, lse)
+
+
+@pytest.mark.parametrize("dtype,path", [("bf16", "mfma"), ("bf16", "valu"), ("f32", "valu")])
+@pytest.mark.parametrize("scale", [0.02, 0.35])
+def test_explicit_softmax_scale(dtype, path, scale):
+    # a small scale (flat weights) and a large one (peaked weights, frequent rebasing)
+    paths, _ = random_trees(900, 2, 33, 8)
+    c = Case(f"scale{scale}_{dtype}_{path}", [700, 96], trees=paths, dtype=dtype,
+             seed=1500 + int(scale * 100))
+    out, lse = c.run(sm_scale=scale, path=path)
+    c.check(out, lse)
+
+
 @pytest.mark.parametrize("N", [64])
 @pytest.mark.parametrize("hq,hkv", [(64, 8), (16, 8)])
 def test_node_chunks(N, hq, hkv):
