@@ -424,44 +424,24 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
     const char* ks = smem + (it % NST) * C::STAGEB;
     const char* vs = ks + C::TILEB;
 
-    // ---- S^T = K Q^T.  Full tiles: step s of key block kb+1 is read right after the last
-    // MFMA that uses step s of block kb, so the reads overlap matrix work without extra
-    // registers.  The shared tile (this wave's turn only) re-reads its K operand after. ----
+    // ---- S^T = K Q^T ----
     f32x4 sacc[TT][KB];
-    {
-      auto read_k = [&](int kb, int s) {
-        const int r = kb * 16 + lr;
-        return *reinterpret_cast<const bf16x8*>(ks + r * C::ROWB +
-                                                (((4 * s + lh) ^ swz_k<C::CH>(r)) << 4));
-      };
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int r = kb * 16 + lr;
       bf16x8 ka[DS];
 #pragma unroll
-      for (int s = 0; s < DS; ++s) ka[s] = read_k(0, s);
+      for (int s = 0; s < DS; ++s)
+        ka[s] = *reinterpret_cast<const bf16x8*>(ks + r * C::ROWB +
+                                                 (((4 * s + lh) ^ swz_k<C::CH>(r)) << 4));
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        f32x4 acc[TN];
+      for (int t = 0; t < TT; ++t) {
+        if (t >= TN && !do_rem) continue;
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < TN; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < DS; ++s) {
-#pragma unroll
-          for (int t = 0; t < TN; ++t)
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s], qreg[t][s], acc[t], 0, 0, 0);
-          if (kb + 1 < KB) ka[s] = read_k(kb + 1, s);
-        }
-#pragma unroll
-        for (int t = 0; t < TN; ++t) sacc[t][kb] = acc[t];
-      }
-      if (RR && do_rem) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < DS; ++s)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_k(kb, s), qreg[TT - 1][s], acc, 0,
-                                                          0, 0);
-          sacc[TT - 1][kb] = acc;
-        }
+        for (int s = 0; s < DS; ++s)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s], qreg[t][s], acc, 0, 0, 0);
+        sacc[t][kb] = acc;
       }
     }
 
