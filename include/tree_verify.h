@@ -188,6 +188,103 @@ size_t tree_verify_attn_workspace_size(const tv_attn_args* a);
  */
 tv_status tree_verify_attn(const tv_attn_args* a, hipStream_t stream);
 
+/*
+ * ---- After the pass: greedy acceptance and the accepted path's KV ----
+ *
+ * Arguments of tree_accept_greedy.  Device memory unless stated; strides in elements.
+ *   dtype                 TV_BF16 or TV_F32 logits.
+ *   B, N, V               requests (>= 0), tree nodes (1..TV_MAX_NODES), vocabulary (>= 1).
+ *   logits [B, N, V]      the target's next-token logits at every node (vocabulary
+ *                         contiguous); lg_sb, lg_sn strides of request and node (>= 0).
+ *   tokens [B, N]         the draft token of every node (node 0, the root, is not read);
+ *                         tokens_sb its request stride (0 = one row for all requests).
+ *   parent [B, N]         the tree (parent_sb 0 = one tree for all requests); must satisfy
+ *                         the parent-before-child convention above.
+ * Outputs (caller-owned device memory, [B, N] int32 unless stated):
+ *   target                the target's greedy token after each node: argmax over the
+ *                         vocabulary, lowest index on ties, the first NaN if a row holds one.
+ *   accepted              the accepted nodes, root first, then -1.
+ *   emitted               the emitted tokens (accepted drafts, then the correction or bonus
+ *                         token), then -1.
+ *   num_accepted [B]      A = number of accepted nodes = number of emitted tokens, 1..depth+1.
+ */
+typedef struct {
+  tv_dtype dtype;
+  int32_t B, N, V;
+  const void* logits;
+  int64_t lg_sb, lg_sn;
+  const int32_t* tokens;
+  int32_t tokens_sb;
+  const int32_t* parent;
+  int32_t parent_sb;
+  int32_t* target;
+  int32_t* accepted;
+  int32_t* emitted;
+  int32_t* num_accepted;
+} tv_accept_args;
+
+/*
+ * tree_accept_greedy -- greedy verification of the tree ("Tree attention mask for
+ * draft-tree verification", "A strong answer": the greedy walk; "Tree Verification",
+ * "Accepting on a Tree").  Per node, the target's greedy token; then, per request, the
+ * walk from the root: at the current node the greedy token is emitted and the first child
+ * (in node order) whose draft token equals it is accepted and becomes the current node;
+ * the walk stops when no child matches (correction) or at a leaf (bonus).  Enqueues an
+ * argmax kernel (one workgroup per node row, HBM-bound on the logits) and a walk kernel
+ * (one lane per request) on `stream`.  Errors: TV_ERR_INVALID_ARG (null pointers, sizes,
+ * strides < V for lg_sn, misaligned logits for the given dtype), TV_ERR_HIP.  B == 0 is a
+ * no-op.
+ */
+tv_status tree_accept_greedy(const tv_accept_args* a, hipStream_t stream);
+
+/*
+ * Arguments of tree_kv_compact.  The KV cache as in tv_attn_args (contiguous or paged;
+ * k and v are written in place) and, per request:
+ *   prefix_len [B]        L before the verified tree (tree node i sits at logical L + i);
+ *                         clamped on the device to [0, max_prefix_len], the host bound
+ *                         the KV buffers are sized for (as in tv_attn_args).
+ *   parent [B, N]         the tree (parent_sb 0 = shared), used to validate the list.
+ *   accepted [B, N]       accepted nodes, root first (as tree_accept_greedy writes them).
+ *   num_accepted [B]      A (entries past A are not read).
+ * Outputs (device, optional -- may be NULL):
+ *   new_len [B]           L + A, the cache length after the step.
+ *   status [B]            0: moved; 1: the list is not a root path of the tree (A < 1 or
+ *                         > N, accepted[0] != 0, an entry out of range, or an entry that is
+ *                         not a child of the one before it) -- nothing of that request moves.
+ */
+typedef struct {
+  tv_dtype dtype;
+  int32_t B, N, Hkv, D;
+  tv_kv_layout kv_layout;
+  void* k;
+  void* v;
+  int64_t kv_sb, kv_st, kv_sh;
+  const int32_t* page_table;
+  int32_t page_size, pages_per_seq;
+  const int32_t* prefix_len;
+  int32_t max_prefix_len;
+  const int32_t* parent;
+  int32_t parent_sb;
+  const int32_t* accepted;
+  const int32_t* num_accepted;
+  int32_t* new_len;
+  int32_t* status;
+} tv_compact_args;
+
+/*
+ * tree_kv_compact -- move the accepted path's KV rows to consecutive positions ("Tree
+ * attention mask for draft-tree verification", "What it costs": node KV was written in
+ * node order, so the accepted entries move to contiguous positions before the next step;
+ * "Tree Verification", "The Cost Side": everything off the surviving path is rolled
+ * back).  For every request and kv head, the K and V rows of accepted node a_j move from
+ * logical position L + a_j to L + j, j < A; rows at or past L + A are left as they are
+ * (the new cache length excludes them).  All source rows of a (request, kv head) are read
+ * before any is written, so overlapping moves are safe.  One workgroup per (kv head,
+ * request) on `stream`.  Errors: TV_ERR_INVALID_ARG (as tree_verify_attn's KV checks),
+ * TV_ERR_UNSUPPORTED (D not 64 or 128), TV_ERR_HIP.  B == 0 is a no-op.
+ */
+tv_status tree_kv_compact(const tv_compact_args* a, hipStream_t stream);
+
 /* Static string naming a status code. */
 const char* tv_status_string(tv_status s);
 
@@ -199,6 +296,10 @@ int32_t tv_abi_version(void);
 
 /* sizeof(tv_attn_args) as compiled into the library, for bindings to check their mirror. */
 size_t tv_attn_args_sizeof(void);
+
+/* sizeof(tv_accept_args) and sizeof(tv_compact_args), likewise. */
+size_t tv_accept_args_sizeof(void);
+size_t tv_compact_args_sizeof(void);
 
 #ifdef __cplusplus
 }

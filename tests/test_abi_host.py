@@ -226,3 +226,73 @@ def test_meta_from_parent_argument_checks():
     assert L.tree_meta_from_parent(1 << 20, 5, 4, 10, None, None, None, None, None) == 1
     assert L.tree_meta_from_parent(None, 0, 4, 10, None, None, None, None, None) == 1
     assert L.tree_meta_from_parent(None, 0, 0, 10, None, None, None, None, None) == 0
+
+
+# ------------------------------------------------- acceptance / compaction checks ----
+def base_accept_args(**kw):
+    a = tv.TvAcceptArgs()
+    a.dtype, a.B, a.N, a.V = 0, 2, 10, 1000
+    fake = 1 << 20  # never dereferenced: every case below fails validation first
+    a.logits = a.tokens = a.parent = fake
+    a.target = a.accepted = a.emitted = a.num_accepted = fake
+    a.lg_sb, a.lg_sn = 10 * 1000, 1000
+    a.tokens_sb = a.parent_sb = 10
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw", [
+    dict(N=0), dict(N=65), dict(V=0), dict(B=-1), dict(dtype=5), dict(logits=None),
+    dict(tokens=None), dict(parent=None), dict(target=None), dict(accepted=None),
+    dict(emitted=None), dict(num_accepted=None), dict(lg_sn=999), dict(lg_sb=5000),
+    dict(tokens_sb=3), dict(parent_sb=9), dict(logits=(1 << 20) + 1),
+])
+def test_accept_argument_checks(kw):
+    L = tv.lib()
+    assert L.tree_accept_greedy(ctypes.byref(base_accept_args(**kw)), None) == 1
+    assert L.tv_last_error().decode() != ""
+
+
+def test_accept_empty_batch_is_noop():
+    a = base_accept_args(B=0, logits=None, tokens=None, parent=None, target=None)
+    assert tv.lib().tree_accept_greedy(ctypes.byref(a), None) == 0
+
+
+def base_compact_args(**kw):
+    a = tv.TvCompactArgs()
+    a.dtype, a.B, a.N, a.Hkv, a.D = 0, 2, 10, 8, 128
+    fake = 1 << 20
+    a.k = a.v = a.prefix_len = a.parent = a.accepted = a.num_accepted = fake
+    a.kv_sb, a.kv_st, a.kv_sh = 100 * 8 * 128, 8 * 128, 128
+    a.parent_sb = 10
+    a.max_prefix_len = 64
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=0), 1), (dict(N=65), 1), (dict(Hkv=0), 1), (dict(D=96), 5), (dict(B=-1), 1),
+    (dict(dtype=4), 1), (dict(kv_layout=2), 1), (dict(k=None), 1), (dict(v=None), 1),
+    (dict(prefix_len=None), 1), (dict(parent=None), 1), (dict(accepted=None), 1),
+    (dict(num_accepted=None), 1), (dict(kv_st=-8), 1), (dict(kv_sh=4), 1),
+    (dict(k=(1 << 20) + 8), 1), (dict(parent_sb=5), 1), (dict(max_prefix_len=-1), 1),
+    (dict(kv_layout=1), 1),
+    (dict(kv_layout=1, page_table=1 << 20, page_size=16, pages_per_seq=4), 1),
+])
+def test_compact_argument_checks(kw, status):
+    L = tv.lib()
+    assert L.tree_kv_compact(ctypes.byref(base_compact_args(**kw)), None) == status
+    assert L.tv_last_error().decode() != ""
+
+
+def test_compact_empty_batch_is_noop():
+    a = base_compact_args(B=0, k=None, v=None, prefix_len=None)
+    assert tv.lib().tree_kv_compact(ctypes.byref(a), None) == 0
+
+
+def test_after_pass_struct_sizes():
+    L = tv.lib()
+    assert L.tv_accept_args_sizeof() == ctypes.sizeof(tv.TvAcceptArgs)
+    assert L.tv_compact_args_sizeof() == ctypes.sizeof(tv.TvCompactArgs)

@@ -5,6 +5,7 @@ builder) behind the C ABI declared in ``include/tree_verify.h``; this package is
 Python binding plus the seeded workload generators used by the tests and the benchmark.
 """
 from ._binding import (  # noqa: F401
-    EXPORTS, LIB_PATH, MAX_NODES, PackedTrees, TreeVerifyError, TvAttnArgs, lib,
-    make_args, tree_meta_build, tree_meta_build_batch, tree_meta_from_parent, tree_verify_attn,
-    tree_verify_attn_workspace_size)
+    EXPORTS, LIB_PATH, MAX_NODES, PackedTrees, TreeVerifyError, TvAcceptArgs, TvAttnArgs,
+    TvCompactArgs, lib, make_accept_args, make_args, make_compact_args, tree_accept_greedy,
+    tree_kv_compact, tree_meta_build, tree_meta_build_batch, tree_meta_from_parent,
+    tree_verify_attn, tree_verify_attn_workspace_size)

@@ -23,9 +23,10 @@ PATHS = {"auto": 0, "valu": 1, "mfma": 2}
 MAX_NODES = 64
 
 # Every symbol include/tree_verify.h declares.
-EXPORTS = ["tree_meta_build", "tree_meta_build_batch", "tree_meta_from_parent", "tree_verify_attn_workspace_size",
-           "tree_verify_attn", "tv_status_string", "tv_last_error", "tv_abi_version",
-           "tv_attn_args_sizeof"]
+EXPORTS = ["tree_meta_build", "tree_meta_build_batch", "tree_meta_from_parent",
+           "tree_verify_attn_workspace_size", "tree_verify_attn", "tree_accept_greedy",
+           "tree_kv_compact", "tv_status_string", "tv_last_error", "tv_abi_version",
+           "tv_attn_args_sizeof", "tv_accept_args_sizeof", "tv_compact_args_sizeof"]
 
 
 class TreeVerifyError(RuntimeError):
@@ -59,6 +60,35 @@ class TvAttnArgs(ctypes.Structure):
     ]
 
 
+class TvAcceptArgs(ctypes.Structure):
+    """Mirror of ``tv_accept_args``."""
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("B", ctypes.c_int32), ("N", ctypes.c_int32),
+        ("V", ctypes.c_int32), ("logits", ctypes.c_void_p),
+        ("lg_sb", ctypes.c_int64), ("lg_sn", ctypes.c_int64),
+        ("tokens", ctypes.c_void_p), ("tokens_sb", ctypes.c_int32),
+        ("parent", ctypes.c_void_p), ("parent_sb", ctypes.c_int32),
+        ("target", ctypes.c_void_p), ("accepted", ctypes.c_void_p),
+        ("emitted", ctypes.c_void_p), ("num_accepted", ctypes.c_void_p),
+    ]
+
+
+class TvCompactArgs(ctypes.Structure):
+    """Mirror of ``tv_compact_args``."""
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("B", ctypes.c_int32), ("N", ctypes.c_int32),
+        ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32), ("kv_layout", ctypes.c_int32),
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("kv_sb", ctypes.c_int64), ("kv_st", ctypes.c_int64), ("kv_sh", ctypes.c_int64),
+        ("page_table", ctypes.c_void_p),
+        ("page_size", ctypes.c_int32), ("pages_per_seq", ctypes.c_int32),
+        ("prefix_len", ctypes.c_void_p), ("max_prefix_len", ctypes.c_int32),
+        ("parent", ctypes.c_void_p), ("parent_sb", ctypes.c_int32),
+        ("accepted", ctypes.c_void_p), ("num_accepted", ctypes.c_void_p),
+        ("new_len", ctypes.c_void_p), ("status", ctypes.c_void_p),
+    ]
+
+
 _LIB = None
 
 
@@ -89,6 +119,12 @@ def lib():
     L.tv_last_error.argtypes = []
     L.tv_abi_version.restype = i32
     L.tv_attn_args_sizeof.restype = ctypes.c_size_t
+    L.tree_accept_greedy.restype = i32
+    L.tree_accept_greedy.argtypes = [ctypes.POINTER(TvAcceptArgs), vp]
+    L.tree_kv_compact.restype = i32
+    L.tree_kv_compact.argtypes = [ctypes.POINTER(TvCompactArgs), vp]
+    L.tv_accept_args_sizeof.restype = ctypes.c_size_t
+    L.tv_compact_args_sizeof.restype = ctypes.c_size_t
     _LIB = L
     return L
 
@@ -296,3 +332,120 @@ def tree_verify_attn(q, k, v, parent, prefix_len, max_prefix_len, *, page_table=
 
 def default_scale(D):
     return 1.0 / math.sqrt(D)
+
+
+# ------------------------------------------------------------ after the pass --------
+def _rows(t, name, B, N):
+    """Request stride of an int32 [B, N] (or shared [N]) tensor."""
+    torch = _torch()
+    if t.dtype != torch.int32:
+        raise ValueError(f"{name} must be int32")
+    if t.dim() == 1:
+        if t.shape[0] != N:
+            raise ValueError(f"{name} must have N entries")
+        return 0
+    if tuple(t.shape) != (B, N) or t.stride(1) != 1:
+        raise ValueError(f"{name} must be [B, N] with contiguous rows")
+    return t.stride(0)
+
+
+def make_accept_args(logits, tokens, parent, target, accepted, emitted, num_accepted):
+    torch = _torch()
+    B, N, V = logits.shape
+    a = TvAcceptArgs()
+    if logits.dtype == torch.bfloat16:
+        a.dtype = TV_BF16
+    elif logits.dtype == torch.float32:
+        a.dtype = TV_F32
+    else:
+        raise ValueError("logits must be bfloat16 or float32")
+    if logits.stride(2) != 1:
+        raise ValueError("logits must be contiguous along the vocabulary")
+    a.B, a.N, a.V = B, N, V
+    a.logits = logits.data_ptr()
+    a.lg_sb, a.lg_sn = logits.stride(0), logits.stride(1)
+    a.tokens_sb = _rows(tokens, "tokens", B, N)
+    a.tokens = tokens.data_ptr()
+    a.parent_sb = _rows(parent, "parent", B, N)
+    a.parent = parent.data_ptr()
+    for t, n in ((target, "target"), (accepted, "accepted"), (emitted, "emitted")):
+        if t.dtype != torch.int32 or tuple(t.shape) != (B, N) or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous int32 [B, N] tensor")
+    if num_accepted.dtype != torch.int32 or tuple(num_accepted.shape) != (B,):
+        raise ValueError("num_accepted must be int32 [B]")
+    a.target, a.accepted = target.data_ptr(), accepted.data_ptr()
+    a.emitted, a.num_accepted = emitted.data_ptr(), num_accepted.data_ptr()
+    return a
+
+
+def tree_accept_greedy(logits, tokens, parent, target=None, accepted=None, emitted=None,
+                       num_accepted=None, stream=None):
+    """Greedy verification: ``logits`` [B, N, V] (bf16 or fp32), draft ``tokens`` and
+    ``parent`` int32 [B, N] (or [N] shared).  Returns ``(target, accepted, emitted,
+    num_accepted)``: the target's greedy token per node, the accepted nodes (root first,
+    -1 padded), the emitted tokens (-1 padded) and their count per request."""
+    torch = _torch()
+    _require_cuda(logits, tokens, parent, target, accepted, emitted, num_accepted)
+    B, N, _ = logits.shape
+    dev = logits.device
+    def mk(t, shape):
+        return torch.empty(shape, dtype=torch.int32, device=dev) if t is None else t
+    target, accepted = mk(target, (B, N)), mk(accepted, (B, N))
+    emitted, num_accepted = mk(emitted, (B, N)), mk(num_accepted, (B,))
+    a = make_accept_args(logits, tokens, parent, target, accepted, emitted, num_accepted)
+    _check(lib().tree_accept_greedy(ctypes.byref(a), _stream(stream)))
+    return target, accepted, emitted, num_accepted
+
+
+def make_compact_args(k, v, prefix_len, max_prefix_len, parent, accepted, num_accepted,
+                      page_table=None, page_size=0, new_len=None, status=None):
+    torch = _torch()
+    a = TvCompactArgs()
+    if k.dtype == torch.bfloat16:
+        a.dtype = TV_BF16
+    elif k.dtype == torch.float32:
+        a.dtype = TV_F32
+    else:
+        raise ValueError("k must be bfloat16 or float32")
+    if k.stride() != v.stride() or k.dtype != v.dtype:
+        raise ValueError("k and v must share dtype and strides")
+    B = prefix_len.shape[0]
+    N = accepted.shape[1]
+    a.B, a.N, a.Hkv, a.D = B, N, k.shape[2], k.shape[3]
+    a.k, a.v = k.data_ptr(), v.data_ptr()
+    a.kv_sb, a.kv_st, a.kv_sh = k.stride(0), k.stride(1), k.stride(2)
+    if page_table is not None:
+        a.kv_layout = TV_KV_PAGED
+        a.page_table = page_table.data_ptr()
+        a.page_size = int(page_size) if page_size else k.shape[1]
+        a.pages_per_seq = page_table.shape[1]
+    else:
+        a.kv_layout = TV_KV_CONTIGUOUS
+    a.prefix_len = prefix_len.data_ptr()
+    a.max_prefix_len = int(max_prefix_len)
+    a.parent_sb = _rows(parent, "parent", B, N)
+    a.parent = parent.data_ptr()
+    if _rows(accepted, "accepted", B, N) != N:
+        raise ValueError("accepted must be a contiguous [B, N] tensor")
+    a.accepted = accepted.data_ptr()
+    a.num_accepted = num_accepted.data_ptr()
+    a.new_len = new_len.data_ptr() if new_len is not None else None
+    a.status = status.data_ptr() if status is not None else None
+    return a
+
+
+def tree_kv_compact(k, v, prefix_len, max_prefix_len, parent, accepted, num_accepted, *,
+                    page_table=None, page_size=0, new_len=None, status=None, stream=None):
+    """Move the accepted path's K/V rows to consecutive positions, in place (contiguous
+    [B, S, Hkv, D] or paged pools with ``page_table``).  Returns ``(new_len, status)``
+    int32 [B] tensors (allocated when not given)."""
+    torch = _torch()
+    _require_cuda(k, v, prefix_len, parent, accepted, num_accepted, page_table, new_len, status)
+    B = prefix_len.shape[0]
+    dev = k.device
+    new_len = torch.empty(B, dtype=torch.int32, device=dev) if new_len is None else new_len
+    status = torch.empty(B, dtype=torch.int32, device=dev) if status is None else status
+    a = make_compact_args(k, v, prefix_len, max_prefix_len, parent, accepted, num_accepted,
+                          page_table, page_size, new_len, status)
+    _check(lib().tree_kv_compact(ctypes.byref(a), _stream(stream)))
+    return new_len, status

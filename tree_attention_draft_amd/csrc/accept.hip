@@ -1,0 +1,228 @@
+// After the verification pass: greedy acceptance on the tree and the compaction of the
+// accepted path's KV rows (gfx950).
+//
+// Semantics ("Tree attention mask for draft-tree verification", "A strong answer" (the
+// greedy walk) and "What it costs" (accepted KV moved to consecutive positions); "Tree
+// Verification", "Accepting on a Tree" and "The Cost Side"):
+//   target[i]  = argmax over the vocabulary of the target's logits after node i (lowest
+//                index on ties, the first NaN if the row holds one);
+//   walk       = from the root, emit target[node]; accept the first child (node order)
+//                whose draft token equals it and continue there; stop when none does;
+//   compaction = K/V row L + a_j -> L + j for the accepted nodes a_0 = 0, a_1, ...
+#include "kernels_common.h"
+
+namespace tv {
+
+// (value, index) candidates of an argmax; `better` is the total order the reduction uses:
+// NaN beats numbers, larger beats smaller, and the lower index breaks ties.
+struct ArgBest {
+  float v;
+  int i;
+};
+
+__device__ inline bool better(const ArgBest& a, const ArgBest& b) {
+  const bool an = a.v != a.v, bn = b.v != b.v;
+  if (an != bn) return an;
+  if (!an && a.v != b.v) return a.v > b.v;
+  return a.i < b.i;
+}
+
+__device__ inline ArgBest wave_best(ArgBest x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    ArgBest y;
+    y.v = __shfl_xor(x.v, off);
+    y.i = __shfl_xor(x.i, off);
+    if (better(y, x)) x = y;
+  }
+  return x;
+}
+
+template <typename T>
+__device__ inline float load_f(const T* p) {
+  return static_cast<float>(*p);
+}
+
+// One workgroup (256 threads) per (request, node) row.  16-byte loads when the row is
+// aligned for them (`vec`), element loads otherwise; each thread keeps its best candidate,
+// then a wave shuffle reduction and one LDS step across the 4 waves.
+template <typename T>
+__global__ void __launch_bounds__(256) tv_argmax_kernel(const T* __restrict__ logits,
+                                                        int64_t sb, int64_t sn, int N, int V,
+                                                        int32_t* __restrict__ target, bool vec) {
+  constexpr int E = 16 / sizeof(T);  // elements per 16-byte load
+  const int row = blockIdx.x;
+  const int b = row / N, n = row % N;
+  const T* x = logits + (int64_t)b * sb + (int64_t)n * sn;
+  ArgBest best{-INFINITY, 0x7fffffff};
+  bool any = false;
+  const int tid = threadIdx.x;
+  int done = 0;
+  if (vec) {
+    const int nv = V / E;
+    const uint4* xv = reinterpret_cast<const uint4*>(x);
+#pragma unroll 4
+    for (int k = tid; k < nv; k += 256) {
+      const uint4 w = xv[k];
+      const T* e = reinterpret_cast<const T*>(&w);
+#pragma unroll
+      for (int t = 0; t < E; ++t) {
+        const ArgBest c{static_cast<float>(e[t]), k * E + t};
+        if (!any || better(c, best)) best = c;
+        any = true;
+      }
+    }
+    done = nv * E;
+  }
+  for (int k = done + tid; k < V; k += 256) {
+    const ArgBest c{load_f(x + k), k};
+    if (!any || better(c, best)) best = c;
+    any = true;
+  }
+  best = wave_best(best);
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const int w = tid >> 6;
+  if ((tid & 63) == 0) {
+    sv[w] = best.v;
+    si[w] = best.i;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    ArgBest r{sv[0], si[0]};
+    for (int k = 1; k < 4; ++k) {
+      const ArgBest c{sv[k], si[k]};
+      if (better(c, r)) r = c;
+    }
+    target[(int64_t)b * N + n] = r.i;
+  }
+}
+
+// One lane per request: the greedy walk.  Children of a node have larger indices
+// (parent-before-child order), so each step moves strictly forward and the walk ends
+// within N steps whatever the parent array holds.
+__global__ void tv_walk_kernel(int B, int N, const int32_t* __restrict__ tokens, int tokens_sb,
+                               const int32_t* __restrict__ parent, int parent_sb,
+                               const int32_t* __restrict__ target,
+                               int32_t* __restrict__ accepted, int32_t* __restrict__ emitted,
+                               int32_t* __restrict__ num_accepted) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const int32_t* par = parent + (int64_t)b * parent_sb;
+  const int32_t* tok = tokens + (int64_t)b * tokens_sb;
+  const int32_t* tg = target + (int64_t)b * N;
+  int32_t* acc = accepted + (int64_t)b * N;
+  int32_t* em = emitted + (int64_t)b * N;
+  int node = 0, a = 0;
+  for (;;) {
+    const int want = tg[node];
+    acc[a] = node;
+    em[a] = want;
+    ++a;
+    int nxt = -1;
+    for (int c = node + 1; c < N; ++c) {
+      if (par[c] == node && tok[c] == want) {
+        nxt = c;
+        break;
+      }
+    }
+    if (nxt < 0 || a >= N) break;
+    node = nxt;
+  }
+  for (int j = a; j < N; ++j) {
+    acc[j] = -1;
+    em[j] = -1;
+  }
+  num_accepted[b] = a;
+}
+
+// Element offset of logical row t of request b, kv head h (contiguous or paged).
+__device__ inline int64_t compact_row(const CompactParams& p, int b, int t, int h) {
+  if (!p.paged) return (int64_t)b * p.kv_sb + (int64_t)t * p.kv_st + (int64_t)h * p.kv_sh;
+  const int page = p.page_table[(int64_t)b * p.pages_per_seq + t / p.page_size];
+  return (int64_t)page * p.kv_sb + (int64_t)(t % p.page_size) * p.kv_st + (int64_t)h * p.kv_sh;
+}
+
+// One workgroup per (kv head, request): validate the accepted list, stage every source
+// row of K and V in LDS, then write them to their new positions (so moves that overlap
+// their own sources are safe).  Rows already in place (a_j == j) are skipped.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) tv_compact_kernel(CompactParams p) {
+  constexpr int E = 16 / sizeof(T);   // elements per 16-byte chunk
+  constexpr int CPR = D / E;          // chunks per row
+  __shared__ uint4 stage[2][TV_MAX_NODES][CPR];
+  __shared__ int32_t acc_s[TV_MAX_NODES];
+  __shared__ int ok_s;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int A = p.num_accepted[b];
+  const int32_t* par = p.parent + (int64_t)b * p.parent_sb;
+  const int32_t* acc = p.accepted + (int64_t)b * p.N;
+  if (tid == 0) {
+    bool ok = A >= 1 && A <= p.N && acc[0] == 0;
+    for (int j = 1; ok && j < A; ++j) {
+      const int a = acc[j];
+      ok = a > 0 && a < p.N && par[a] == acc[j - 1];
+    }
+    ok_s = ok;
+    if (h == 0) {
+      if (p.status) p.status[b] = ok ? 0 : 1;
+      const int L0 = min(max(p.prefix_len[b], 0), p.max_prefix_len);
+      if (p.new_len) p.new_len[b] = ok ? L0 + A : L0;
+    }
+  }
+  if (tid < TV_MAX_NODES) acc_s[tid] = (tid < A && tid < p.N) ? acc[tid] : tid;
+  __syncthreads();
+  if (!ok_s) return;
+  const int L = min(max(p.prefix_len[b], 0), p.max_prefix_len);
+  char* kbase = static_cast<char*>(p.k);
+  char* vbase = static_cast<char*>(p.v);
+  // read: rows j in [1, A) that move
+  for (int it = tid; it < A * CPR * 2; it += 256) {
+    const int kv = it / (A * CPR), rem = it % (A * CPR);
+    const int j = rem / CPR, c = rem % CPR;
+    if (acc_s[j] == j) continue;
+    const int64_t off = compact_row(p, b, L + acc_s[j], h) * sizeof(T) + c * 16;
+    stage[kv][j][c] = *reinterpret_cast<const uint4*>((kv ? vbase : kbase) + off);
+  }
+  __syncthreads();
+  for (int it = tid; it < A * CPR * 2; it += 256) {
+    const int kv = it / (A * CPR), rem = it % (A * CPR);
+    const int j = rem / CPR, c = rem % CPR;
+    if (acc_s[j] == j) continue;
+    const int64_t off = compact_row(p, b, L + j, h) * sizeof(T) + c * 16;
+    *reinterpret_cast<uint4*>((kv ? vbase : kbase) + off) = stage[kv][j][c];
+  }
+}
+
+hipError_t launch_argmax(const AcceptParams& p, hipStream_t s) {
+  const dim3 grid(p.B * p.N);
+  if (p.bf16)
+    hipLaunchKernelGGL(tv_argmax_kernel<__bf16>, grid, dim3(256), 0, s,
+                       static_cast<const __bf16*>(p.logits), p.lg_sb, p.lg_sn, p.N, p.V,
+                       p.target, p.vec);
+  else
+    hipLaunchKernelGGL(tv_argmax_kernel<float>, grid, dim3(256), 0, s,
+                       static_cast<const float*>(p.logits), p.lg_sb, p.lg_sn, p.N, p.V,
+                       p.target, p.vec);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(tv_walk_kernel, dim3((p.B + 63) / 64), dim3(64), 0, s, p.B, p.N, p.tokens,
+                     p.tokens_sb, p.parent, p.parent_sb, p.target, p.accepted, p.emitted,
+                     p.num_accepted);
+  return hipGetLastError();
+}
+
+hipError_t launch_compact(const CompactParams& p, hipStream_t s) {
+  const dim3 grid(p.Hkv, p.B);
+  if (p.bf16) {
+    if (p.D == 64) hipLaunchKernelGGL((tv_compact_kernel<__bf16, 64>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((tv_compact_kernel<__bf16, 128>), grid, dim3(256), 0, s, p);
+  } else {
+    if (p.D == 64) hipLaunchKernelGGL((tv_compact_kernel<float, 64>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((tv_compact_kernel<float, 128>), grid, dim3(256), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tv

@@ -274,6 +274,132 @@ extern "C" tv_status tree_meta_from_parent(const int32_t* parent, int32_t parent
   return TV_OK;
 }
 
+// ---------------------------------------------------------------- acceptance -------
+namespace tv {
+namespace {
+
+tv_status check_accept(const tv_accept_args* a) {
+  if (!a) return fail(TV_ERR_INVALID_ARG, "args is null");
+  if (a->dtype != TV_BF16 && a->dtype != TV_F32) return fail(TV_ERR_INVALID_ARG, "bad dtype");
+  if (a->B < 0) return fail(TV_ERR_INVALID_ARG, "B < 0");
+  if (a->N < 1 || a->N > TV_MAX_NODES) return fail(TV_ERR_INVALID_ARG, "N outside 1..64");
+  if (a->V < 1) return fail(TV_ERR_INVALID_ARG, "V < 1");
+  if (a->B == 0) return TV_OK;
+  if (!a->logits || !a->tokens || !a->parent || !a->target || !a->accepted || !a->emitted ||
+      !a->num_accepted)
+    return fail(TV_ERR_INVALID_ARG, "null pointer argument");
+  if (a->lg_sn < a->V || a->lg_sb < 0 || (a->B > 1 && a->lg_sb < (int64_t)a->N * a->lg_sn))
+    return fail(TV_ERR_INVALID_ARG, "logits strides must cover [B, N, V] without overlap");
+  if (a->tokens_sb != 0 && a->tokens_sb < a->N)
+    return fail(TV_ERR_INVALID_ARG, "tokens_sb must be 0 or >= N");
+  if (a->parent_sb != 0 && a->parent_sb < a->N)
+    return fail(TV_ERR_INVALID_ARG, "parent_sb must be 0 or >= N");
+  const uintptr_t esz = a->dtype == TV_BF16 ? 2 : 4;
+  if (reinterpret_cast<uintptr_t>(a->logits) % esz != 0)
+    return fail(TV_ERR_INVALID_ARG, "logits not aligned to its element size");
+  return TV_OK;
+}
+
+tv_status check_compact(const tv_compact_args* a) {
+  if (!a) return fail(TV_ERR_INVALID_ARG, "args is null");
+  if (a->dtype != TV_BF16 && a->dtype != TV_F32) return fail(TV_ERR_INVALID_ARG, "bad dtype");
+  if (a->B < 0) return fail(TV_ERR_INVALID_ARG, "B < 0");
+  if (a->N < 1 || a->N > TV_MAX_NODES) return fail(TV_ERR_INVALID_ARG, "N outside 1..64");
+  if (a->Hkv < 1) return fail(TV_ERR_INVALID_ARG, "Hkv < 1");
+  if (a->D != 64 && a->D != 128) return fail(TV_ERR_UNSUPPORTED, "D must be 64 or 128");
+  if (a->kv_layout != TV_KV_CONTIGUOUS && a->kv_layout != TV_KV_PAGED)
+    return fail(TV_ERR_INVALID_ARG, "bad kv_layout");
+  if (a->max_prefix_len < 0 || a->max_prefix_len > (1 << 30))
+    return fail(TV_ERR_INVALID_ARG, "max_prefix_len out of range");
+  if (a->B == 0) return TV_OK;
+  if (!a->k || !a->v || !a->prefix_len || !a->parent || !a->accepted || !a->num_accepted)
+    return fail(TV_ERR_INVALID_ARG, "null pointer argument");
+  if (a->parent_sb != 0 && a->parent_sb < a->N)
+    return fail(TV_ERR_INVALID_ARG, "parent_sb must be 0 or >= N");
+  const int64_t vec = a->dtype == TV_BF16 ? 8 : 4;
+  const int64_t strides[] = {a->kv_sb, a->kv_st, a->kv_sh};
+  for (int64_t st : strides)
+    if (st < 0 || st % vec != 0)
+      return fail(TV_ERR_INVALID_ARG, "strides must be >= 0 and multiples of 16 bytes");
+  if (!aligned16(a->k) || !aligned16(a->v))
+    return fail(TV_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
+  if (a->kv_layout == TV_KV_PAGED) {
+    if (!a->page_table || a->page_size < 1 || a->pages_per_seq < 1)
+      return fail(TV_ERR_INVALID_ARG, "paged KV needs page_table, page_size, pages_per_seq");
+    const int64_t need = ((int64_t)a->max_prefix_len + a->N + a->page_size - 1) / a->page_size;
+    if (a->pages_per_seq < need)
+      return fail(TV_ERR_INVALID_ARG, "pages_per_seq too small for max_prefix_len + N");
+  }
+  return TV_OK;
+}
+
+}  // namespace
+}  // namespace tv
+
+extern "C" tv_status tree_accept_greedy(const tv_accept_args* a, hipStream_t stream) {
+  using namespace tv;
+  tv_status st = check_accept(a);
+  if (st != TV_OK) return st;
+  if (a->B == 0) return TV_OK;
+  AcceptParams p;
+  p.bf16 = a->dtype == TV_BF16;
+  const int64_t esz = p.bf16 ? 2 : 4;
+  p.vec = aligned16(a->logits) && (a->lg_sb * esz) % 16 == 0 && (a->lg_sn * esz) % 16 == 0;
+  p.B = a->B;
+  p.N = a->N;
+  p.V = a->V;
+  p.logits = a->logits;
+  p.lg_sb = a->lg_sb;
+  p.lg_sn = a->lg_sn;
+  p.tokens = a->tokens;
+  p.tokens_sb = a->tokens_sb;
+  p.parent = a->parent;
+  p.parent_sb = a->parent_sb;
+  p.target = a->target;
+  p.accepted = a->accepted;
+  p.emitted = a->emitted;
+  p.num_accepted = a->num_accepted;
+  const hipError_t e = launch_argmax(p, stream);
+  if (e != hipSuccess) return fail(TV_ERR_HIP, hipGetErrorString(e));
+  return TV_OK;
+}
+
+extern "C" tv_status tree_kv_compact(const tv_compact_args* a, hipStream_t stream) {
+  using namespace tv;
+  tv_status st = check_compact(a);
+  if (st != TV_OK) return st;
+  if (a->B == 0) return TV_OK;
+  CompactParams p;
+  p.bf16 = a->dtype == TV_BF16;
+  p.paged = a->kv_layout == TV_KV_PAGED;
+  p.B = a->B;
+  p.N = a->N;
+  p.Hkv = a->Hkv;
+  p.D = a->D;
+  p.k = a->k;
+  p.v = a->v;
+  p.kv_sb = a->kv_sb;
+  p.kv_st = a->kv_st;
+  p.kv_sh = a->kv_sh;
+  p.page_table = a->page_table;
+  p.page_size = a->page_size;
+  p.pages_per_seq = a->pages_per_seq;
+  p.prefix_len = a->prefix_len;
+  p.max_prefix_len = a->max_prefix_len;
+  p.parent = a->parent;
+  p.parent_sb = a->parent_sb;
+  p.accepted = a->accepted;
+  p.num_accepted = a->num_accepted;
+  p.new_len = a->new_len;
+  p.status = a->status;
+  const hipError_t e = launch_compact(p, stream);
+  if (e != hipSuccess) return fail(TV_ERR_HIP, hipGetErrorString(e));
+  return TV_OK;
+}
+
+extern "C" size_t tv_accept_args_sizeof(void) { return sizeof(tv_accept_args); }
+extern "C" size_t tv_compact_args_sizeof(void) { return sizeof(tv_compact_args); }
+
 extern "C" const char* tv_status_string(tv_status s) {
   switch (s) {
     case TV_OK: return "TV_OK";

@@ -53,6 +53,44 @@ struct MfmaShape {
   int tpw, nw, rr, nc;
 };
 
+// Device-side arguments of the acceptance kernels (argmax over the vocabulary, walk).
+struct AcceptParams {
+  bool bf16, vec;  // vec: every logits row is 16-byte aligned
+  int B, N, V;
+  const void* logits;
+  int64_t lg_sb, lg_sn;
+  const int32_t* tokens;
+  int tokens_sb;
+  const int32_t* parent;
+  int parent_sb;
+  int32_t* target;
+  int32_t* accepted;
+  int32_t* emitted;
+  int32_t* num_accepted;
+};
+
+// Device-side arguments of the KV compaction kernel.
+struct CompactParams {
+  bool bf16, paged;
+  int B, N, Hkv, D;
+  void* k;
+  void* v;
+  int64_t kv_sb, kv_st, kv_sh;
+  const int32_t* page_table;
+  int page_size, pages_per_seq;
+  const int32_t* prefix_len;
+  int max_prefix_len;
+  const int32_t* parent;
+  int parent_sb;
+  const int32_t* accepted;
+  const int32_t* num_accepted;
+  int32_t* new_len;
+  int32_t* status;
+};
+
+hipError_t launch_argmax(const AcceptParams& p, hipStream_t s);
+hipError_t launch_compact(const CompactParams& p, hipStream_t s);
+
 hipError_t launch_attn_mfma(const AttnParams& p, int D, MfmaShape shape, hipStream_t s);
 hipError_t launch_attn_valu(const AttnParams& p, int D, bool bf16, hipStream_t s);
 hipError_t launch_merge(const AttnParams& p, int D, bool bf16, hipStream_t s);
