@@ -99,6 +99,112 @@ def cpu_baseline(host, trees_parent, prefix_lens, N, budget_s, page_size=0):
                       f"batch; all nodes and heads), fp64 numpy oracle, {el:.1f} s"}
 
 
+def bench_after_pass(args):
+    """Time the after-pass entry points at the B=64, N=33 batch: greedy acceptance over
+    Llama-3-sized logits (V=128256, bf16; the argmax reads 541 MB), and the accepted-path
+    KV compaction on the L=4096, 8 kv-head, D=128 cache.  One JSON line per stage."""
+    import numpy as np
+    import torch
+
+    import tree_attention_draft_amd as tv
+    from oracle import accept as oacc
+    from oracle import meta as ometa
+    from tree_attention_draft_amd import workloads
+
+    dev = torch.device("cuda:0")
+    spec = workloads.WORKLOADS["b64_l4096_n33"]
+    B, N, Hkv, D, Lp = spec["B"], spec["N"], spec["Hkv"], spec["D"], spec["L"]
+    V = 128256
+    trees, _ = workloads.trees_for(spec)
+    parents = [ometa.build_from_paths(t, 0)["parent"] for t in trees]
+    par = torch.tensor(np.array(parents, np.int32), device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    logits = (torch.randn((B, N, V), generator=g, device=dev) * 3).to(torch.bfloat16)
+    rng = np.random.Generator(np.random.PCG64(1234))
+    # draft tokens that agree with the target along one random root path per request, so
+    # the walk does real work and the compaction has rows to move
+    am = logits.float().argmax(-1).cpu().numpy()
+    tokens = rng.integers(0, V, size=(B, N)).astype(np.int32)
+    for b in range(B):
+        node = 0
+        while True:
+            kids = [c for c in range(N) if parents[b][c] == node]
+            if not kids:
+                break
+            c = kids[int(rng.integers(0, len(kids)))]
+            tokens[b, c] = am[b, node]
+            node = c
+    tok = torch.from_numpy(tokens).to(dev)
+    target = torch.empty((B, N), dtype=torch.int32, device=dev)
+    acc = torch.empty((B, N), dtype=torch.int32, device=dev)
+    em = torch.empty((B, N), dtype=torch.int32, device=dev)
+    na = torch.empty(B, dtype=torch.int32, device=dev)
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for a, b_ in ev:
+            a.record()
+            fn()
+            b_.record()
+        torch.cuda.synchronize()
+        ms = [a.elapsed_time(b_) for a, b_ in ev]
+        return float(np.mean(ms)) / 1e3, [float(np.percentile(ms, x)) * 1e3 for x in (10, 50, 90)]
+
+    t_acc, pct = timed(lambda: tv.tree_accept_greedy(logits, tok, par, target, acc, em, na),
+                       args.steps, args.warmup)
+    # parity against the oracle on two requests
+    want = oacc.argmax_rows(logits[[0, B - 1]].float().cpu().numpy())
+    ok = np.array_equal(target[[0, B - 1]].cpu().numpy(), want)
+    for i, b in enumerate([0, B - 1]):
+        a_ref, e_ref = oacc.accept_greedy(parents[b], tokens[b], want[i])
+        ok &= acc[b, :len(a_ref)].tolist() == a_ref and em[b, :len(e_ref)].tolist() == e_ref
+    abytes = B * N * V * 2 + 4 * B * N * 5 + 4 * B
+    mean_acc = float(na.float().mean())
+    print(json.dumps({
+        "metric": "greedy tree acceptance (argmax over V + walk): verified nodes/s",
+        "value": B * N / t_acc, "unit": "nodes/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": t_acc * 1e3, "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"B={B} requests, N={N}-node random trees, V={V} bf16 "
+                               "logits N(0,9), drafts agreeing along one random path",
+                   "mean_accepted": mean_acc},
+        "roofline": {"bound": "hbm", "achieved": abytes / t_acc / 1e9, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": abytes / t_acc / 1e9 / HBM_PEAK_GBS,
+                     "traffic": None, "kernel": "tv_argmax_kernel + tv_walk_kernel",
+                     "kernel_p10_p50_p90_us": pct, "algorithmic_bytes_per_launch": abytes},
+        "parity": {"requests": [0, B - 1], "ok": bool(ok)}}), flush=True)
+
+    # ---- compaction on the headline cache ----
+    L = np.full(B, Lp, np.int32)
+    S = Lp + N
+    k = torch.randn((B, S, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+    v = torch.randn((B, S, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+    pl = torch.from_numpy(L).to(dev)
+    moved = int(sum(sum(1 for j, a in enumerate(acc[b, :int(na[b])].tolist()) if a != j)
+                    for b in range(B)))
+    t_c, pct_c = timed(lambda: tv.tree_kv_compact(k, v, pl, Lp, par, acc, na), args.steps,
+                       args.warmup)
+    cbytes = moved * Hkv * D * 2 * 2 * 2 + 4 * B * (N * 2 + 3)
+    print(json.dumps({
+        "metric": "accepted-path KV compaction: requests/s",
+        "value": B / t_c, "unit": "requests/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": t_c * 1e3, "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"B={B}, L={Lp}, N={N}, Hkv={Hkv}, D={D} contiguous bf16 KV, "
+                               "accepted lists from the acceptance stage",
+                   "rows_moved": moved},
+        "roofline": {"bound": "hbm", "achieved": cbytes / t_c / 1e9, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": cbytes / t_c / 1e9 / HBM_PEAK_GBS,
+                     "traffic": None, "kernel": "tv_compact_kernel",
+                     "kernel_p10_p50_p90_us": pct_c, "algorithmic_bytes_per_launch": cbytes},
+    }), flush=True)
+
+
 def describe(name, spec, B, N, Lmax, page):
     if name == "b64_l4096_n33" and B == 64:
         return ("tree-verify attention: B=64 requests, prefix L=4096, N=33-node random draft "
@@ -123,12 +229,18 @@ def main():
     ap.add_argument("--workload", default="b64_l4096_n33",
                     help="bf16 workload name (default: the B=64, L=4096, N=33 batch)")
     ap.add_argument("--batch", type=int, default=0, help="override the workload's batch")
+    ap.add_argument("--after-pass", action="store_true",
+                    help="time greedy acceptance and KV compaction instead (two JSON lines)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}, "
               f"WORLD_SIZE={world}); multi-GPU sharding is design-only.", file=sys.stderr)
         sys.exit(2)
+
+    if args.after_pass:
+        bench_after_pass(args)
+        return
 
     import numpy as np
     import torch

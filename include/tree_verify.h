@@ -207,6 +207,8 @@ tv_status tree_verify_attn(const tv_attn_args* a, hipStream_t stream);
  *   emitted               the emitted tokens (accepted drafts, then the correction or bonus
  *                         token), then -1.
  *   num_accepted [B]      A = number of accepted nodes = number of emitted tokens, 1..depth+1.
+ *   workspace             device scratch of at least tree_accept_greedy_workspace_size()
+ *                         bytes, 16-byte aligned (per-row partial maxima); caller-owned.
  */
 typedef struct {
   tv_dtype dtype;
@@ -221,7 +223,12 @@ typedef struct {
   int32_t* accepted;
   int32_t* emitted;
   int32_t* num_accepted;
+  void* workspace;
+  size_t workspace_bytes;
 } tv_accept_args;
+
+/* Bytes of workspace tree_accept_greedy needs for these sizes (pointers are not read). */
+size_t tree_accept_greedy_workspace_size(const tv_accept_args* a);
 
 /*
  * tree_accept_greedy -- greedy verification of the tree ("Tree attention mask for
@@ -229,11 +236,13 @@ typedef struct {
  * "Accepting on a Tree").  Per node, the target's greedy token; then, per request, the
  * walk from the root: at the current node the greedy token is emitted and the first child
  * (in node order) whose draft token equals it is accepted and becomes the current node;
- * the walk stops when no child matches (correction) or at a leaf (bonus).  Enqueues an
- * argmax kernel (one workgroup per node row, HBM-bound on the logits) and a walk kernel
- * (one lane per request) on `stream`.  Errors: TV_ERR_INVALID_ARG (null pointers, sizes,
- * strides < V for lg_sn, misaligned logits for the given dtype), TV_ERR_HIP.  B == 0 is a
- * no-op.
+ * the walk stops when no child matches (correction) or at a leaf (bonus).  Enqueues, on
+ * `stream`, a kernel clearing the per-row partial maxima in the workspace, the argmax
+ * kernel (workgroups over 16K-element slices of every row, HBM-bound on the logits, each
+ * folding its best (value, index) into the row's partial with one 64-bit atomic max) and
+ * the walk kernel (one workgroup per request).  Errors: TV_ERR_INVALID_ARG (null
+ * pointers, sizes, strides < V for lg_sn, misaligned logits for the given dtype),
+ * TV_ERR_WORKSPACE, TV_ERR_HIP.  B == 0 is a no-op.
  */
 tv_status tree_accept_greedy(const tv_accept_args* a, hipStream_t stream);
 

@@ -235,6 +235,7 @@ def base_accept_args(**kw):
     fake = 1 << 20  # never dereferenced: every case below fails validation first
     a.logits = a.tokens = a.parent = fake
     a.target = a.accepted = a.emitted = a.num_accepted = fake
+    a.workspace, a.workspace_bytes = fake, 2 * 10 * 8
     a.lg_sb, a.lg_sn = 10 * 1000, 1000
     a.tokens_sb = a.parent_sb = 10
     for k, v in kw.items():
@@ -252,6 +253,17 @@ def test_accept_argument_checks(kw):
     L = tv.lib()
     assert L.tree_accept_greedy(ctypes.byref(base_accept_args(**kw)), None) == 1
     assert L.tv_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(workspace=None), 6), (dict(workspace_bytes=2 * 10 * 8 - 1), 6),
+    (dict(workspace=(1 << 20) + 4), 1), (dict(B=7000, lg_sb=10 * 1000), 5),
+])
+def test_accept_workspace_checks(kw, status):
+    a = base_accept_args(**kw)
+    L = tv.lib()
+    assert L.tree_accept_greedy(ctypes.byref(a), None) == status
+    assert L.tree_accept_greedy_workspace_size(ctypes.byref(base_accept_args())) == 2 * 10 * 8
 
 
 def test_accept_empty_batch_is_noop():

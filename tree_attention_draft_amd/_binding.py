@@ -25,6 +25,7 @@ MAX_NODES = 64
 # Every symbol include/tree_verify.h declares.
 EXPORTS = ["tree_meta_build", "tree_meta_build_batch", "tree_meta_from_parent",
            "tree_verify_attn_workspace_size", "tree_verify_attn", "tree_accept_greedy",
+           "tree_accept_greedy_workspace_size",
            "tree_kv_compact", "tv_status_string", "tv_last_error", "tv_abi_version",
            "tv_attn_args_sizeof", "tv_accept_args_sizeof", "tv_compact_args_sizeof"]
 
@@ -70,6 +71,7 @@ class TvAcceptArgs(ctypes.Structure):
         ("parent", ctypes.c_void_p), ("parent_sb", ctypes.c_int32),
         ("target", ctypes.c_void_p), ("accepted", ctypes.c_void_p),
         ("emitted", ctypes.c_void_p), ("num_accepted", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -119,6 +121,8 @@ def lib():
     L.tv_last_error.argtypes = []
     L.tv_abi_version.restype = i32
     L.tv_attn_args_sizeof.restype = ctypes.c_size_t
+    L.tree_accept_greedy_workspace_size.restype = ctypes.c_size_t
+    L.tree_accept_greedy_workspace_size.argtypes = [ctypes.POINTER(TvAcceptArgs)]
     L.tree_accept_greedy.restype = i32
     L.tree_accept_greedy.argtypes = [ctypes.POINTER(TvAcceptArgs), vp]
     L.tree_kv_compact.restype = i32
@@ -379,7 +383,7 @@ def make_accept_args(logits, tokens, parent, target, accepted, emitted, num_acce
 
 
 def tree_accept_greedy(logits, tokens, parent, target=None, accepted=None, emitted=None,
-                       num_accepted=None, stream=None):
+                       num_accepted=None, workspace=None, stream=None):
     """Greedy verification: ``logits`` [B, N, V] (bf16 or fp32), draft ``tokens`` and
     ``parent`` int32 [B, N] (or [N] shared).  Returns ``(target, accepted, emitted,
     num_accepted)``: the target's greedy token per node, the accepted nodes (root first,
@@ -393,6 +397,11 @@ def tree_accept_greedy(logits, tokens, parent, target=None, accepted=None, emitt
     target, accepted = mk(target, (B, N)), mk(accepted, (B, N))
     emitted, num_accepted = mk(emitted, (B, N)), mk(num_accepted, (B,))
     a = make_accept_args(logits, tokens, parent, target, accepted, emitted, num_accepted)
+    need = int(lib().tree_accept_greedy_workspace_size(ctypes.byref(a)))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    a.workspace = workspace.data_ptr()
+    a.workspace_bytes = workspace.numel() * workspace.element_size()
     _check(lib().tree_accept_greedy(ctypes.byref(a), _stream(stream)))
     return target, accepted, emitted, num_accepted
 

@@ -43,38 +43,84 @@ __device__ inline float load_f(const T* p) {
   return static_cast<float>(*p);
 }
 
-// One workgroup (256 threads) per (request, node) row.  16-byte loads when the row is
-// aligned for them (`vec`), element loads otherwise; each thread keeps its best candidate,
-// then a wave shuffle reduction and one LDS step across the 4 waves.
+// Order-preserving 64-bit key of an argmax candidate: the high word orders the values
+// (numbers by value with -0 folded onto +0, every NaN above +inf), the low word holds
+// ~index so that among equal values the lower index is larger.  The row's argmax is then
+// the plain unsigned maximum of its candidates' keys.
+__device__ inline uint64_t arg_key(float v, int i) {
+  uint32_t k;
+  if (v != v) {
+    k = 0xffffffffu;
+  } else {
+    const uint32_t u = __float_as_uint(v + 0.0f);  // -0 + 0 = +0
+    k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  }
+  return ((uint64_t)k << 32) | (uint32_t)(~(uint32_t)i);
+}
+
+constexpr int kArgSlice = 16384;  // elements of a row per workgroup
+
+// Clears the per-row partial maxima (a kernel rather than a memset, so the sequence stays
+// safe to capture and replay in a graph).
+__global__ void tv_argmax_init_kernel(uint64_t* __restrict__ part, int rows) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < rows) part[i] = 0ull;
+}
+
+// Workgroup (slice, row): 256 threads scan kArgSlice elements of one row with 16-byte
+// loads when the row is aligned for them (`vec`), element loads otherwise; a vector can
+// change a thread's candidate only if its max beats the current best or it holds a NaN
+// (its sum is then NaN too; an inf - inf sum only sends it down the exact path
+// needlessly).  Thread candidates reduce over the wave with shuffles and over the 4 waves
+// through LDS; lane 0 folds the result into the row's partial with one atomic max.
 template <typename T>
 __global__ void __launch_bounds__(256) tv_argmax_kernel(const T* __restrict__ logits,
                                                         int64_t sb, int64_t sn, int N, int V,
-                                                        int32_t* __restrict__ target, bool vec) {
+                                                        uint64_t* __restrict__ part, bool vec) {
   constexpr int E = 16 / sizeof(T);  // elements per 16-byte load
-  const int row = blockIdx.x;
+  const int row = blockIdx.y;
   const int b = row / N, n = row % N;
   const T* x = logits + (int64_t)b * sb + (int64_t)n * sn;
+  const int lo = blockIdx.x * kArgSlice;
+  const int hi = min(V, lo + kArgSlice);
   ArgBest best{-INFINITY, 0x7fffffff};
   bool any = false;
   const int tid = threadIdx.x;
-  int done = 0;
+  int done = lo;
   if (vec) {
-    const int nv = V / E;
+    const int v0 = lo / E, v1 = hi / E;  // lo is a multiple of E
     const uint4* xv = reinterpret_cast<const uint4*>(x);
-#pragma unroll 4
-    for (int k = tid; k < nv; k += 256) {
-      const uint4 w = xv[k];
-      const T* e = reinterpret_cast<const T*>(&w);
+    constexpr int U = 4;
+    for (int k0 = v0 + tid; k0 < v1; k0 += 256 * U) {
+      uint4 w[U];
 #pragma unroll
-      for (int t = 0; t < E; ++t) {
-        const ArgBest c{static_cast<float>(e[t]), k * E + t};
-        if (!any || better(c, best)) best = c;
-        any = true;
+      for (int u = 0; u < U; ++u)
+        if (k0 + 256 * u < v1) w[u] = xv[k0 + 256 * u];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = k0 + 256 * u;
+        if (k >= v1) break;
+        const T* e = reinterpret_cast<const T*>(&w[u]);
+        float mx = static_cast<float>(e[0]), sm = mx;
+#pragma unroll
+        for (int t = 1; t < E; ++t) {
+          const float f = static_cast<float>(e[t]);
+          mx = fmaxf(mx, f);
+          sm += f;
+        }
+        if (!any || mx > best.v || sm != sm) {
+#pragma unroll
+          for (int t = 0; t < E; ++t) {
+            const ArgBest c{static_cast<float>(e[t]), k * E + t};
+            if (!any || better(c, best)) best = c;
+            any = true;
+          }
+        }
       }
     }
-    done = nv * E;
+    done = v1 * E;
   }
-  for (int k = done + tid; k < V; k += 256) {
+  for (int k = done + tid; k < hi; k += 256) {
     const ArgBest c{load_f(x + k), k};
     if (!any || better(c, best)) best = c;
     any = true;
@@ -94,46 +140,66 @@ __global__ void __launch_bounds__(256) tv_argmax_kernel(const T* __restrict__ lo
       const ArgBest c{sv[k], si[k]};
       if (better(c, r)) r = c;
     }
-    target[(int64_t)b * N + n] = r.i;
+    if (r.i < hi) atomicMax(reinterpret_cast<unsigned long long*>(part + row),
+                            (unsigned long long)arg_key(r.v, r.i));
   }
 }
 
-// One lane per request: the greedy walk.  Children of a node have larger indices
+// One workgroup per request: the tree, the draft tokens and the greedy tokens are staged
+// in LDS by N lanes, then lane 0 walks.  Children of a node have larger indices
 // (parent-before-child order), so each step moves strictly forward and the walk ends
 // within N steps whatever the parent array holds.
-__global__ void tv_walk_kernel(int B, int N, const int32_t* __restrict__ tokens, int tokens_sb,
-                               const int32_t* __restrict__ parent, int parent_sb,
-                               const int32_t* __restrict__ target,
-                               int32_t* __restrict__ accepted, int32_t* __restrict__ emitted,
-                               int32_t* __restrict__ num_accepted) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= B) return;
-  const int32_t* par = parent + (int64_t)b * parent_sb;
-  const int32_t* tok = tokens + (int64_t)b * tokens_sb;
-  const int32_t* tg = target + (int64_t)b * N;
-  int32_t* acc = accepted + (int64_t)b * N;
-  int32_t* em = emitted + (int64_t)b * N;
-  int node = 0, a = 0;
-  for (;;) {
-    const int want = tg[node];
-    acc[a] = node;
-    em[a] = want;
-    ++a;
-    int nxt = -1;
-    for (int c = node + 1; c < N; ++c) {
-      if (par[c] == node && tok[c] == want) {
-        nxt = c;
-        break;
+__global__ void __launch_bounds__(64) tv_walk_kernel(int B, int N,
+                                                     const int32_t* __restrict__ tokens,
+                                                     int tokens_sb,
+                                                     const int32_t* __restrict__ parent,
+                                                     int parent_sb,
+                                                     const uint64_t* __restrict__ part,
+                                                     int32_t* __restrict__ target,
+                                                     int32_t* __restrict__ accepted,
+                                                     int32_t* __restrict__ emitted,
+                                                     int32_t* __restrict__ num_accepted) {
+  __shared__ int32_t par[TV_MAX_NODES], tok[TV_MAX_NODES], tg[TV_MAX_NODES];
+  __shared__ int32_t acc[TV_MAX_NODES], em[TV_MAX_NODES];
+  __shared__ int na;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tid < N) {
+    par[tid] = parent[(int64_t)b * parent_sb + tid];
+    tok[tid] = tokens[(int64_t)b * tokens_sb + tid];
+    // the row's argmax index is the complement of the low word of its partial
+    tg[tid] = (int32_t)~(uint32_t)(part[(int64_t)b * N + tid] & 0xffffffffull);
+    target[(int64_t)b * N + tid] = tg[tid];
+    acc[tid] = -1;
+    em[tid] = -1;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int node = 0, a = 0;
+    for (;;) {
+      const int want = tg[node];
+      acc[a] = node;
+      em[a] = want;
+      ++a;
+      int nxt = -1;
+      for (int c = node + 1; c < N; ++c) {
+        if (par[c] == node && tok[c] == want) {
+          nxt = c;
+          break;
+        }
       }
+      if (nxt < 0 || a >= N) break;
+      node = nxt;
     }
-    if (nxt < 0 || a >= N) break;
-    node = nxt;
+    na = a;
   }
-  for (int j = a; j < N; ++j) {
-    acc[j] = -1;
-    em[j] = -1;
+  __syncthreads();
+  if (tid < N) {
+    accepted[(int64_t)b * N + tid] = acc[tid];
+    emitted[(int64_t)b * N + tid] = em[tid];
   }
-  num_accepted[b] = a;
+  if (tid == 0) num_accepted[b] = na;
+  (void)B;
 }
 
 // Element offset of logical row t of request b, kv head h (contiguous or paged).
@@ -196,19 +262,25 @@ __global__ void __launch_bounds__(256) tv_compact_kernel(CompactParams p) {
 }
 
 hipError_t launch_argmax(const AcceptParams& p, hipStream_t s) {
-  const dim3 grid(p.B * p.N);
-  if (p.bf16)
-    hipLaunchKernelGGL(tv_argmax_kernel<__bf16>, grid, dim3(256), 0, s,
-                       static_cast<const __bf16*>(p.logits), p.lg_sb, p.lg_sn, p.N, p.V,
-                       p.target, p.vec);
-  else
-    hipLaunchKernelGGL(tv_argmax_kernel<float>, grid, dim3(256), 0, s,
-                       static_cast<const float*>(p.logits), p.lg_sb, p.lg_sn, p.N, p.V,
-                       p.target, p.vec);
+  const int rows = p.B * p.N;
+  uint64_t* part = static_cast<uint64_t*>(p.workspace);
+  hipLaunchKernelGGL(tv_argmax_init_kernel, dim3((rows + 255) / 256), dim3(256), 0, s, part,
+                     rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(tv_walk_kernel, dim3((p.B + 63) / 64), dim3(64), 0, s, p.B, p.N, p.tokens,
-                     p.tokens_sb, p.parent, p.parent_sb, p.target, p.accepted, p.emitted,
+  const dim3 grid((p.V + kArgSlice - 1) / kArgSlice, rows);
+  if (p.bf16)
+    hipLaunchKernelGGL(tv_argmax_kernel<__bf16>, grid, dim3(256), 0, s,
+                       static_cast<const __bf16*>(p.logits), p.lg_sb, p.lg_sn, p.N, p.V, part,
+                       p.vec);
+  else
+    hipLaunchKernelGGL(tv_argmax_kernel<float>, grid, dim3(256), 0, s,
+                       static_cast<const float*>(p.logits), p.lg_sb, p.lg_sn, p.N, p.V, part,
+                       p.vec);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(tv_walk_kernel, dim3(p.B), dim3(64), 0, s, p.B, p.N, p.tokens,
+                     p.tokens_sb, p.parent, p.parent_sb, part, p.target, p.accepted, p.emitted,
                      p.num_accepted);
   return hipGetLastError();
 }

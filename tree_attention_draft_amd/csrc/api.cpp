@@ -297,6 +297,12 @@ tv_status check_accept(const tv_accept_args* a) {
   const uintptr_t esz = a->dtype == TV_BF16 ? 2 : 4;
   if (reinterpret_cast<uintptr_t>(a->logits) % esz != 0)
     return fail(TV_ERR_INVALID_ARG, "logits not aligned to its element size");
+  if (a->V > (1 << 30)) return fail(TV_ERR_INVALID_ARG, "V > 2^30");
+  if ((int64_t)a->B * a->N > 65535) return fail(TV_ERR_UNSUPPORTED, "B * N > 65535");
+  const size_t need = (size_t)a->B * a->N * 8;
+  if (!a->workspace || a->workspace_bytes < need)
+    return fail(TV_ERR_WORKSPACE, "workspace missing or smaller than required");
+  if (!aligned16(a->workspace)) return fail(TV_ERR_INVALID_ARG, "workspace not 16-byte aligned");
   return TV_OK;
 }
 
@@ -359,6 +365,7 @@ extern "C" tv_status tree_accept_greedy(const tv_accept_args* a, hipStream_t str
   p.accepted = a->accepted;
   p.emitted = a->emitted;
   p.num_accepted = a->num_accepted;
+  p.workspace = a->workspace;
   const hipError_t e = launch_argmax(p, stream);
   if (e != hipSuccess) return fail(TV_ERR_HIP, hipGetErrorString(e));
   return TV_OK;
@@ -395,6 +402,11 @@ extern "C" tv_status tree_kv_compact(const tv_compact_args* a, hipStream_t strea
   const hipError_t e = launch_compact(p, stream);
   if (e != hipSuccess) return fail(TV_ERR_HIP, hipGetErrorString(e));
   return TV_OK;
+}
+
+extern "C" size_t tree_accept_greedy_workspace_size(const tv_accept_args* a) {
+  if (!a || a->B < 0 || a->N < 1 || a->N > TV_MAX_NODES) return 0;
+  return (size_t)a->B * a->N * 8;
 }
 
 extern "C" size_t tv_accept_args_sizeof(void) { return sizeof(tv_accept_args); }

@@ -67,6 +67,7 @@ struct AcceptParams {
   int32_t* accepted;
   int32_t* emitted;
   int32_t* num_accepted;
+  void* workspace;  // B*N uint64 per-row partial maxima
 };
 
 // Device-side arguments of the KV compaction kernel.
