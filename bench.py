@@ -204,6 +204,27 @@ def bench_after_pass(args):
                      "kernel_p10_p50_p90_us": pct_c, "algorithmic_bytes_per_launch": cbytes},
     }), flush=True)
 
+    # ---- tree-budget plan (host C++), one plan per batch size of a serving sweep ----
+    ridge = tv.tree_ridge_tokens(2.5e15, HBM_PEAK_GBS * 1e9, 2.0)
+    probs = [0.62, 0.18, 0.07, 0.03]
+    batches = [1, 2, 4, 8, 16, 32, 64, 128]
+    reps = 200
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        plans = [tv.tree_budget_plan(b, ridge, probs, 64, 8) for b in batches]
+    t_p = (time.perf_counter() - t0) / (reps * len(batches))
+    print(json.dumps({
+        "metric": "tree-budget plan (host): plans/s", "value": 1.0 / t_p, "unit": "plans/s",
+        "n_gpus": 0, "steps": reps * len(batches), "warmup": 0, "ms_per_step": t_p * 1e3,
+        "higher_is_better": True, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": "best static tree for batches 1..128 on MI355X's ridge "
+                               f"({ridge:.1f} tokens), rank probabilities {probs}, "
+                               "at most 64 nodes, depth <= 8, through the Python binding",
+                   "nodes_by_batch": {str(b): p[0] for b, p in zip(batches, plans)},
+                   "expected_tokens_by_batch": {str(b): round(p[2], 4)
+                                                for b, p in zip(batches, plans)}},
+        "roofline": None}), flush=True)
+
 
 def describe(name, spec, B, N, Lmax, page):
     if name == "b64_l4096_n33" and B == 64:

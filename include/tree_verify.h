@@ -294,6 +294,79 @@ typedef struct {
  */
 tv_status tree_kv_compact(const tv_compact_args* a, hipStream_t stream);
 
+/*
+ * Tree-budget policy (host arithmetic only; every pointer below is host memory, caller
+ * owned; nothing is allocated on the device and no stream is used).
+ *
+ * Acceptance model ("Tree attention mask for draft-tree verification", "What it buys"):
+ * rank_prob[r] is the probability that the target's greedy token is the drafter's rank-r
+ * candidate (each in [0, 1], sum <= 1, 1 <= num_ranks <= 4096; ranks >= num_ranks have
+ * probability 0).  A node is reached with the product of its ranks' probabilities along
+ * its path from the root.
+ */
+
+/*
+ * tree_expected_tokens -- expected tokens per step of one tree under greedy verification:
+ * 1 + the sum over non-root nodes of their reach probability ("What it buys").
+ *   parent[n]  parent convention of the header comment (n >= 1, no upper limit here);
+ *   rank[n]    node i's drafter rank among its siblings (>= 0, distinct among siblings;
+ *              rank[0] is not read);
+ *   reach[n]   optional output (may be NULL): each node's reach probability, 1 at the root;
+ *   *expected  output.
+ * Errors: TV_ERR_INVALID_ARG (NULL, n < 1, a parent violation, negative or repeated
+ * sibling rank, probabilities outside [0, 1] or summing above 1).
+ */
+tv_status tree_expected_tokens(const int32_t* parent, const int32_t* rank, int32_t n,
+                               const double* rank_prob, int32_t num_ranks, double* reach,
+                               double* expected);
+
+/*
+ * tree_ridge_tokens -- tokens per step at which a decode step turns from bandwidth- to
+ * compute-bound ("What it costs": dense flops over HBM bandwidth, for two-byte weights):
+ * *ridge = peak_flops * bytes_per_weight / (2 * hbm_bytes_per_s).  All inputs finite, > 0.
+ */
+tv_status tree_ridge_tokens(double peak_flops, double hbm_bytes_per_s, double bytes_per_weight,
+                            double* ridge);
+
+/*
+ * tree_budget_nodes -- the tree size a batch can afford: the largest N with
+ * batch * N <= ridge_tokens, clamped to [1, max_nodes] ("What it costs": break-even batch =
+ * ridge / N; trees shrink toward a chain, and at the ridge to the root alone, as the batch
+ * grows).  Errors: TV_ERR_INVALID_ARG (batch < 1, max_nodes < 1, ridge negative or not
+ * finite, nodes NULL).
+ */
+tv_status tree_budget_nodes(int32_t batch, double ridge_tokens, int32_t max_nodes,
+                            int32_t* nodes);
+
+/*
+ * tree_best_static -- the tree of at most `nodes` nodes (root included, 1..TV_MAX_NODES)
+ * and depth <= max_depth (1..63) with the most expected tokens ("Tree Verification", "The
+ * Cost Side": a node is worth its path product, so spend nodes where the acceptance mass
+ * is).  Since a path's product never exceeds its parent's, the nodes - 1 rank paths of
+ * largest product form a tree; ties go to the shorter, then the lexicographically smaller
+ * path; paths of product 0 are never taken (so fewer paths may come back).
+ * Output (host, caller-owned): the chosen rank paths in the CSR form tree_meta_build reads
+ * -- ranks[path_off[p] .. path_off[p+1]) -- in (length, lexicographic) order, i.e. the
+ * builder's node order; path_off needs nodes entries, ranks ranks_cap entries
+ * ((nodes - 1) * max_depth always suffices); *num_paths = paths returned; *expected (may
+ * be NULL) = their expected tokens per step.
+ * Errors: TV_ERR_INVALID_ARG (NULL outputs, bad probabilities or depth),
+ *         TV_ERR_CAPACITY (nodes outside 1..64, or ranks_cap too small).
+ */
+tv_status tree_best_static(const double* rank_prob, int32_t num_ranks, int32_t nodes,
+                           int32_t max_depth, int32_t* ranks, int64_t ranks_cap,
+                           int64_t* path_off, int32_t* num_paths, double* expected);
+
+/*
+ * tree_budget_plan -- tree_budget_nodes (max_nodes clamped to TV_MAX_NODES) followed by
+ * tree_best_static of that size: the static tree a batch of `batch` requests should
+ * verify.  *nodes (may be NULL) receives the size; other outputs as tree_best_static.
+ */
+tv_status tree_budget_plan(int32_t batch, double ridge_tokens, int32_t max_nodes,
+                           const double* rank_prob, int32_t num_ranks, int32_t max_depth,
+                           int32_t* nodes, int32_t* ranks, int64_t ranks_cap, int64_t* path_off,
+                           int32_t* num_paths, double* expected);
+
 /* Static string naming a status code. */
 const char* tv_status_string(tv_status s);
 

@@ -26,7 +26,9 @@ MAX_NODES = 64
 EXPORTS = ["tree_meta_build", "tree_meta_build_batch", "tree_meta_from_parent",
            "tree_verify_attn_workspace_size", "tree_verify_attn", "tree_accept_greedy",
            "tree_accept_greedy_workspace_size",
-           "tree_kv_compact", "tv_status_string", "tv_last_error", "tv_abi_version",
+           "tree_kv_compact", "tree_expected_tokens", "tree_ridge_tokens",
+           "tree_budget_nodes", "tree_best_static", "tree_budget_plan",
+           "tv_status_string", "tv_last_error", "tv_abi_version",
            "tv_attn_args_sizeof", "tv_accept_args_sizeof", "tv_compact_args_sizeof"]
 
 
@@ -129,6 +131,17 @@ def lib():
     L.tree_kv_compact.argtypes = [ctypes.POINTER(TvCompactArgs), vp]
     L.tv_accept_args_sizeof.restype = ctypes.c_size_t
     L.tv_compact_args_sizeof.restype = ctypes.c_size_t
+    f64, i64 = ctypes.c_double, ctypes.c_int64
+    L.tree_expected_tokens.restype = i32
+    L.tree_expected_tokens.argtypes = [vp, vp, i32, vp, i32, vp, vp]
+    L.tree_ridge_tokens.restype = i32
+    L.tree_ridge_tokens.argtypes = [f64, f64, f64, vp]
+    L.tree_budget_nodes.restype = i32
+    L.tree_budget_nodes.argtypes = [i32, f64, i32, vp]
+    L.tree_best_static.restype = i32
+    L.tree_best_static.argtypes = [vp, i32, i32, i32, vp, i64, vp, vp, vp]
+    L.tree_budget_plan.restype = i32
+    L.tree_budget_plan.argtypes = [i32, f64, i32, vp, i32, i32, vp, vp, i64, vp, vp, vp]
     _LIB = L
     return L
 
@@ -458,3 +471,80 @@ def tree_kv_compact(k, v, prefix_len, max_prefix_len, parent, accepted, num_acce
                           page_table, page_size, new_len, status)
     _check(lib().tree_kv_compact(ctypes.byref(a), _stream(stream)))
     return new_len, status
+
+
+# ------------------------------------------------------------------ budget policy ----
+def _probs(rank_prob):
+    pr = np.ascontiguousarray(rank_prob, dtype=np.float64)
+    if pr.ndim != 1:
+        raise ValueError("rank_prob must be one-dimensional")
+    return pr
+
+
+def tree_expected_tokens(parent, rank, rank_prob):
+    """Expected tokens per step of one tree under greedy verification.  Returns
+    ``(expected, reach)`` with ``reach`` the per-node reach probabilities."""
+    par = np.ascontiguousarray(parent, dtype=np.int32)
+    rk = np.ascontiguousarray(rank, dtype=np.int32)
+    if par.shape != rk.shape or par.ndim != 1:
+        raise ValueError("parent and rank must be one-dimensional and of equal length")
+    pr = _probs(rank_prob)
+    reach = np.empty(max(par.size, 1), np.float64)
+    out = ctypes.c_double(0.0)
+    _check(lib().tree_expected_tokens(par.ctypes.data, rk.ctypes.data, par.size,
+                                      pr.ctypes.data, pr.size, reach.ctypes.data,
+                                      ctypes.byref(out)))
+    return out.value, reach[:par.size].copy()
+
+
+def tree_ridge_tokens(peak_flops, hbm_bytes_per_s, bytes_per_weight=2.0):
+    """Tokens per step at which a decode step turns compute-bound."""
+    out = ctypes.c_double(0.0)
+    _check(lib().tree_ridge_tokens(float(peak_flops), float(hbm_bytes_per_s),
+                                   float(bytes_per_weight), ctypes.byref(out)))
+    return out.value
+
+
+def tree_budget_nodes(batch, ridge_tokens, max_nodes=MAX_NODES):
+    """Largest tree size N with batch * N <= ridge, within [1, max_nodes]."""
+    out = ctypes.c_int32(0)
+    _check(lib().tree_budget_nodes(int(batch), float(ridge_tokens), int(max_nodes),
+                                   ctypes.byref(out)))
+    return out.value
+
+
+def _paths_from_csr(ranks, path_off, k):
+    return [tuple(int(x) for x in ranks[path_off[i]:path_off[i + 1]]) for i in range(k)]
+
+
+def tree_best_static(rank_prob, nodes, max_depth):
+    """Best static tree of at most ``nodes`` nodes.  Returns ``(paths, expected)``, the
+    rank paths in the builder's node order."""
+    pr = _probs(rank_prob)
+    cap = max(1, (int(nodes) - 1) * int(max_depth))
+    ranks = np.empty(cap, np.int32)
+    path_off = np.empty(max(1, int(nodes)), np.int64)
+    k = ctypes.c_int32(0)
+    e = ctypes.c_double(0.0)
+    _check(lib().tree_best_static(pr.ctypes.data, pr.size, int(nodes), int(max_depth),
+                                  ranks.ctypes.data, cap, path_off.ctypes.data,
+                                  ctypes.byref(k), ctypes.byref(e)))
+    return _paths_from_csr(ranks, path_off, k.value), e.value
+
+
+def tree_budget_plan(batch, ridge_tokens, rank_prob, max_nodes=MAX_NODES, max_depth=8):
+    """Tree size for the batch and the best static tree of that size.  Returns
+    ``(nodes, paths, expected)``."""
+    pr = _probs(rank_prob)
+    n_cap = max(1, min(int(max_nodes), MAX_NODES))
+    cap = max(1, (n_cap - 1) * int(max_depth))
+    ranks = np.empty(cap, np.int32)
+    path_off = np.empty(n_cap, np.int64)
+    n = ctypes.c_int32(0)
+    k = ctypes.c_int32(0)
+    e = ctypes.c_double(0.0)
+    _check(lib().tree_budget_plan(int(batch), float(ridge_tokens), int(max_nodes),
+                                  pr.ctypes.data, pr.size, int(max_depth), ctypes.byref(n),
+                                  ranks.ctypes.data, cap, path_off.ctypes.data,
+                                  ctypes.byref(k), ctypes.byref(e)))
+    return n.value, _paths_from_csr(ranks, path_off, k.value), e.value
