@@ -71,10 +71,19 @@ def request_kv(host, b, T, page_size):
     return oattn.bf16_bits_to_f64(k), oattn.bf16_bits_to_f64(v)
 
 
-def cpu_baseline(host, trees_parent, prefix_lens, N, budget_s, page_size=0):
-    """Time the fp64 oracle (as it stands) on whole requests until the budget is spent."""
-    import numpy as np
+def oracle_request(host, b, parent, L, N, page_size, rope_theta):
+    """The oracle's (out, lse) of request b (fused rotary embedding when rope_theta > 0)."""
     from oracle import attn as oattn
+    from oracle import rope as orope
+    q = oattn.bf16_bits_to_f64(host["q"][b])
+    k, v = request_kv(host, b, int(L) + N, page_size)
+    if rope_theta > 0:
+        return orope.tree_attention_request_rope(q, k, v, parent, int(L), rope_theta)
+    return oattn.tree_attention_request(q, k, v, parent, int(L))
+
+
+def cpu_baseline(host, trees_parent, prefix_lens, N, budget_s, page_size=0, rope_theta=0.0):
+    """Time the fp64 oracle (as it stands) on whole requests until the budget is spent."""
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()
@@ -87,10 +96,7 @@ def cpu_baseline(host, trees_parent, prefix_lens, N, budget_s, page_size=0):
     # whole requests in batch order, cycling over the batch until the budget is spent
     while time.perf_counter() - t0 < budget_s:
         b = done % B
-        T = int(prefix_lens[b]) + N
-        q = oattn.bf16_bits_to_f64(host["q"][b])
-        k, v = request_kv(host, b, T, page_size)
-        oattn.tree_attention_request(q, k, v, trees_parent[b], int(prefix_lens[b]))
+        oracle_request(host, b, trees_parent[b], prefix_lens[b], N, page_size, rope_theta)
         done += 1
     el = time.perf_counter() - t0
     return {"value": done * N / el, "unit": "nodes/s", "cores": int(threads),
@@ -250,6 +256,8 @@ def main():
     ap.add_argument("--workload", default="b64_l4096_n33",
                     help="bf16 workload name (default: the B=64, L=4096, N=33 batch)")
     ap.add_argument("--batch", type=int, default=0, help="override the workload's batch")
+    ap.add_argument("--rope-theta", type=float, default=0.0,
+                    help="> 0: time the pass with the rotary embedding fused in")
     ap.add_argument("--after-pass", action="store_true",
                     help="time greedy acceptance and KV compaction instead (two JSON lines)")
     args = ap.parse_args()
@@ -335,7 +343,8 @@ def main():
         qi, ki, vi = qkv[i % n_copies]
         ev_a[i].record()
         tv.tree_verify_attn(qi, ki, vi, parent_dev[s], prefix_dev, Lmax, page_table=pt_dev,
-                            page_size=page, out=out, lse=lse, workspace=ws)
+                            page_size=page, out=out, lse=lse, workspace=ws,
+                            rope_theta=args.rope_theta)
         ev_b[i].record()
 
     print("[bench] warmup", file=sys.stderr, flush=True)
@@ -360,10 +369,7 @@ def main():
     worst = 0.0
     sample = [0, B - 1]
     for b in sample:
-        T = int(L[b]) + N
-        kb, vb = request_kv(host, b, T, page)
-        o, l = oattn.tree_attention_request(oattn.bf16_bits_to_f64(host["q"][b]), kb, vb,
-                                            ref_parent[b], int(L[b]))
+        o, l = oracle_request(host, b, ref_parent[b], L[b], N, page, args.rope_theta)
         worst = max(worst, float(np.abs(out_h[b] - o).max()), float(np.abs(lse_h[b] - l).max()))
     parity_ok = worst <= 2e-2
 
@@ -379,7 +385,8 @@ def main():
     flops = algorithmic_flops(L, depths, Hq, D)
     achieved = alg_bytes / kern_avg_s / 1e9
     traffic = None
-    if args.workload == "b64_l4096_n33" and not args.batch and os.path.exists(COUNTERS):
+    if (args.workload == "b64_l4096_n33" and not args.batch and not args.rope_theta
+            and os.path.exists(COUNTERS)):
         with open(COUNTERS) as fh:
             c = json.load(fh)
         if c.get("kernel_source_hash") == kernel_source_hash():
@@ -403,6 +410,7 @@ def main():
             "B": B, "L": Lmax, "N": N, "Hq": Hq, "Hkv": Hkv, "D": D,
             "kv_layout": f"paged{page}" if page else "contiguous", "splits": "auto",
             "workspace_bytes": ws_bytes,
+            **({"rope_theta": args.rope_theta} if args.rope_theta else {}),
         },
         "roofline": {
             "bound": "hbm",
@@ -424,7 +432,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(host, ref_parent, L, N, args.cpu_seconds, page)
+        result["cpu_baseline"] = cpu_baseline(host, ref_parent, L, N, args.cpu_seconds, page,
+                                              args.rope_theta)
     print(json.dumps(result), flush=True)
     if not parity_ok:
         sys.exit(1)

@@ -35,7 +35,7 @@ extern "C" {
 #endif
 
 #define TV_MAX_NODES 64
-#define TV_ABI_VERSION 1
+#define TV_ABI_VERSION 2
 
 typedef enum {
   TV_OK = 0,
@@ -139,6 +139,15 @@ tv_status tree_meta_from_parent(const int32_t* parent, int32_t parent_sb, int32_
  *   num_splits: 0 = automatic, else the number of key-range splits per (request, kv head).
  *   path: TV_PATH_AUTO picks the MFMA kernel for bf16 once N * (Hq / Hkv) >= 16, else the
  *        VALU kernel; the others force one (MFMA needs bf16).
+ *   rope_theta: 0 = no rotary embedding (q and every key are used as given).  > 0 fuses
+ *        the rotary embedding into the pass ("Tree attention mask for draft-tree
+ *        verification", "What interviewers probe next" and "Common mistakes": node i sits
+ *        at position L + depth(i), siblings share one): q and the tree keys
+ *        (tokens L .. L+N-1) are given UNROTATED and are rotated inside the kernels at
+ *        L + depth(i); prefix keys (t < L) are taken as already rotated at t.  Rotate-half
+ *        form: features (m, m + D/2), m < D/2, turn by angle pos * rope_theta^(-2m/D)
+ *        (angle reduced in fp64, cos/sin in fp32).  Nothing is written back: the tree rows
+ *        stay unrotated in the cache until tree_kv_compact rotates the accepted ones.
  */
 typedef struct tv_attn_args {
   int32_t dtype;           /* tv_dtype of q, k, v and out                                  */
@@ -164,6 +173,7 @@ typedef struct tv_attn_args {
   size_t workspace_bytes;
   int32_t num_splits;
   int32_t path;            /* tv_path                                                       */
+  double rope_theta;       /* 0: none; > 0: fused rotary embedding at L + depth (above)     */
 } tv_attn_args;
 
 /*
@@ -260,6 +270,12 @@ tv_status tree_accept_greedy(const tv_accept_args* a, hipStream_t stream);
  *   status [B]            0: moved; 1: the list is not a root path of the tree (A < 1 or
  *                         > N, accepted[0] != 0, an entry out of range, or an entry that is
  *                         not a child of the one before it) -- nothing of that request moves.
+ *   rope_theta            0: rows move unchanged.  > 0: the companion of tree_verify_attn's
+ *                         fused rotary embedding -- the tree keys are unrotated in the cache,
+ *                         and accepted node a_j's key is written to L + j rotated at
+ *                         position L + j (= L + depth(a_j)), rows already in place included,
+ *                         so every cached key is then rotated at its position.  Values move
+ *                         unchanged.
  */
 typedef struct {
   tv_dtype dtype;
@@ -278,6 +294,7 @@ typedef struct {
   const int32_t* num_accepted;
   int32_t* new_len;
   int32_t* status;
+  double rope_theta;
 } tv_compact_args;
 
 /*

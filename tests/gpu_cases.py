@@ -7,6 +7,7 @@ import numpy as np
 import tree_attention_draft_amd as tv
 from oracle import attn as oattn
 from oracle import meta as ometa
+from oracle import rope as orope
 from tree_attention_draft_amd import workloads
 
 TOL = {"bf16": 2e-2, "f32": 1e-5}
@@ -39,6 +40,7 @@ class Case:
         assert all(len(p) == self.N for p in self.parent_gpu)
         self.page_size = page_size
         self.sm_scale = None  # the oracle's default (1/sqrt(D)) unless a run sets one
+        self.rope_theta = 0.0  # fused rotary embedding of the last run (0: none)
         say(name, f"B={self.B} N={self.N} Hq={Hq} Hkv={Hkv} D={D} {dtype} "
             f"L=[{self.L.min() if self.B else 0},{self.L.max() if self.B else 0}] "
             f"paged={page_size} seed={seed}")
@@ -74,8 +76,10 @@ class Case:
         parent = kw.pop("parent", d["parent"])
         if kw.get("sm_scale"):
             self.sm_scale = float(kw["sm_scale"])
+        self.rope_theta = float(kw.get("rope_theta", 0.0))
         say(self.name, "tree_verify_attn", {k: v for k, v in kw.items()
-                                            if k in ("num_splits", "path", "max_prefix_len")})
+                                            if k in ("num_splits", "path", "max_prefix_len",
+                                                     "rope_theta")})
         out, lse = tv.tree_verify_attn(d["q"], d["k"], d["v"], parent, d["prefix_len"], **kw)
         torch.cuda.synchronize()
         return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
@@ -100,6 +104,10 @@ class Case:
 
     def oracle(self, b):
         q, k, v = self.request_inputs(b)
+        if self.rope_theta > 0:
+            return orope.tree_attention_request_rope(q, k, v, self.parent_oracle[b],
+                                                     int(self.L[b]), self.rope_theta,
+                                                     sm_scale=self.sm_scale)
         return oattn.tree_attention_request(q, k, v, self.parent_oracle[b], int(self.L[b]),
                                             sm_scale=self.sm_scale)
 

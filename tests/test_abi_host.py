@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_struct_and_version():
     L = tv.lib()
-    assert L.tv_abi_version() == 1
+    assert L.tv_abi_version() == 2
     assert L.tv_attn_args_sizeof() == ctypes.sizeof(TvAttnArgs)
     for code in range(8):
         assert L.tv_status_string(code).decode().startswith("TV_")
@@ -180,7 +180,8 @@ def base_args(**kw):
     (dict(sm_scale=float("inf")), 1), (dict(num_splits=-2), 1), (dict(path=9), 1),
     (dict(path=2, dtype=1), 5), (dict(kv_layout=1), 1),
     (dict(kv_layout=1, page_table=1 << 20, page_size=16, pages_per_seq=4), 1),
-    (dict(kv_layout=3), 1),
+    (dict(kv_layout=3), 1), (dict(rope_theta=-1.0), 1), (dict(rope_theta=float("nan")), 1),
+    (dict(rope_theta=float("inf")), 1),
 ])
 def test_attn_argument_checks(kw, status):
     a = base_args(**kw)
@@ -292,6 +293,7 @@ def base_compact_args(**kw):
     (dict(k=(1 << 20) + 8), 1), (dict(parent_sb=5), 1), (dict(max_prefix_len=-1), 1),
     (dict(kv_layout=1), 1),
     (dict(kv_layout=1, page_table=1 << 20, page_size=16, pages_per_seq=4), 1),
+    (dict(rope_theta=-2.0), 1), (dict(rope_theta=float("nan")), 1),
 ])
 def test_compact_argument_checks(kw, status):
     L = tv.lib()

@@ -60,6 +60,7 @@ class TvAttnArgs(ctypes.Structure):
         ("lse", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("num_splits", ctypes.c_int32), ("path", ctypes.c_int32),
+        ("rope_theta", ctypes.c_double),
     ]
 
 
@@ -90,6 +91,7 @@ class TvCompactArgs(ctypes.Structure):
         ("parent", ctypes.c_void_p), ("parent_sb", ctypes.c_int32),
         ("accepted", ctypes.c_void_p), ("num_accepted", ctypes.c_void_p),
         ("new_len", ctypes.c_void_p), ("status", ctypes.c_void_p),
+        ("rope_theta", ctypes.c_double),
     ]
 
 
@@ -269,7 +271,8 @@ def tree_meta_from_parent(parent, prefix_len=None, batch=None, depth=None, bitma
 
 
 def make_args(q, k, v, parent, prefix_len, max_prefix_len, page_table=None, page_size=0,
-              sm_scale=0.0, out=None, lse=None, workspace=None, num_splits=0, path="auto"):
+              sm_scale=0.0, out=None, lse=None, workspace=None, num_splits=0, path="auto",
+              rope_theta=0.0):
     """Fill a TvAttnArgs from torch tensors (no allocation, no checks beyond shapes)."""
     torch = _torch()
     B, N, Hq, D = q.shape
@@ -312,6 +315,7 @@ def make_args(q, k, v, parent, prefix_len, max_prefix_len, page_table=None, page
         a.workspace_bytes = workspace.numel() * workspace.element_size()
     a.num_splits = int(num_splits)
     a.path = PATHS[path] if isinstance(path, str) else int(path)
+    a.rope_theta = float(rope_theta)
     return a
 
 
@@ -322,11 +326,13 @@ def tree_verify_attn_workspace_size(q, k, v, parent, prefix_len, max_prefix_len,
 
 def tree_verify_attn(q, k, v, parent, prefix_len, max_prefix_len, *, page_table=None,
                      page_size=0, sm_scale=0.0, out=None, lse=None, workspace=None,
-                     num_splits=0, path="auto", stream=None):
+                     num_splits=0, path="auto", rope_theta=0.0, stream=None):
     """Tree-verification attention.  q [B, N, Hq, D]; k, v [B, S, Hkv, D] (contiguous) or
     [pages, page_size, Hkv, D] with ``page_table`` [B, pages_per_seq]; parent int32 [B, N]
-    or [N]; prefix_len int32 [B].  Returns ``(out, lse)``; ``lse`` is the natural-log
-    log-sum-exp per (request, node, query head)."""
+    or [N]; prefix_len int32 [B].  ``rope_theta`` > 0 fuses the rotary embedding: q and
+    the tree keys are passed unrotated and rotated at L + depth inside the kernels.
+    Returns ``(out, lse)``; ``lse`` is the natural-log log-sum-exp per (request, node,
+    query head)."""
     torch = _torch()
     _require_cuda(q, k, v, parent, prefix_len, page_table, out, lse, workspace)
     B, N, Hq, D = q.shape
@@ -336,7 +342,8 @@ def tree_verify_attn(q, k, v, parent, prefix_len, max_prefix_len, *, page_table=
         lse = torch.empty((B, N, Hq), dtype=torch.float32, device=q.device)
     a = make_args(q, k, v, parent, prefix_len, max_prefix_len, page_table=page_table,
                   page_size=page_size, sm_scale=sm_scale, out=out, lse=lse,
-                  workspace=workspace, num_splits=num_splits, path=path)
+                  workspace=workspace, num_splits=num_splits, path=path,
+                  rope_theta=rope_theta)
     need = int(lib().tree_verify_attn_workspace_size(ctypes.byref(a)))
     if need > 0 and (workspace is None or a.workspace_bytes < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -420,9 +427,11 @@ def tree_accept_greedy(logits, tokens, parent, target=None, accepted=None, emitt
 
 
 def make_compact_args(k, v, prefix_len, max_prefix_len, parent, accepted, num_accepted,
-                      page_table=None, page_size=0, new_len=None, status=None):
+                      page_table=None, page_size=0, new_len=None, status=None,
+                      rope_theta=0.0):
     torch = _torch()
     a = TvCompactArgs()
+    a.rope_theta = float(rope_theta)
     if k.dtype == torch.bfloat16:
         a.dtype = TV_BF16
     elif k.dtype == torch.float32:
@@ -457,10 +466,13 @@ def make_compact_args(k, v, prefix_len, max_prefix_len, parent, accepted, num_ac
 
 
 def tree_kv_compact(k, v, prefix_len, max_prefix_len, parent, accepted, num_accepted, *,
-                    page_table=None, page_size=0, new_len=None, status=None, stream=None):
+                    page_table=None, page_size=0, new_len=None, status=None,
+                    rope_theta=0.0, stream=None):
     """Move the accepted path's K/V rows to consecutive positions, in place (contiguous
-    [B, S, Hkv, D] or paged pools with ``page_table``).  Returns ``(new_len, status)``
-    int32 [B] tensors (allocated when not given)."""
+    [B, S, Hkv, D] or paged pools with ``page_table``).  ``rope_theta`` > 0 also rotates
+    every accepted key at its new position (the companion of the fused rotary embedding
+    of ``tree_verify_attn``).  Returns ``(new_len, status)`` int32 [B] tensors (allocated
+    when not given)."""
     torch = _torch()
     _require_cuda(k, v, prefix_len, parent, accepted, num_accepted, page_table, new_len, status)
     B = prefix_len.shape[0]
@@ -468,7 +480,7 @@ def tree_kv_compact(k, v, prefix_len, max_prefix_len, parent, accepted, num_acce
     new_len = torch.empty(B, dtype=torch.int32, device=dev) if new_len is None else new_len
     status = torch.empty(B, dtype=torch.int32, device=dev) if status is None else status
     a = make_compact_args(k, v, prefix_len, max_prefix_len, parent, accepted, num_accepted,
-                          page_table, page_size, new_len, status)
+                          page_table, page_size, new_len, status, rope_theta)
     _check(lib().tree_kv_compact(ctypes.byref(a), _stream(stream)))
     return new_len, status
 

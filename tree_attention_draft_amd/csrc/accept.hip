@@ -211,7 +211,9 @@ __device__ inline int64_t compact_row(const CompactParams& p, int b, int t, int 
 
 // One workgroup per (kv head, request): validate the accepted list, stage every source
 // row of K and V in LDS, then write them to their new positions (so moves that overlap
-// their own sources are safe).  Rows already in place (a_j == j) are skipped.
+// their own sources are safe).  Rows already in place (a_j == j) are skipped, except the
+// keys when the rotary embedding is fused (p.rope): then every accepted key is written
+// rotated at its new position L + j, pairs (m, m + D/2) being chunks c and c + CPR/2.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) tv_compact_kernel(CompactParams p) {
   constexpr int E = 16 / sizeof(T);   // elements per 16-byte chunk
@@ -243,11 +245,11 @@ __global__ void __launch_bounds__(256) tv_compact_kernel(CompactParams p) {
   const int L = min(max(p.prefix_len[b], 0), p.max_prefix_len);
   char* kbase = static_cast<char*>(p.k);
   char* vbase = static_cast<char*>(p.v);
-  // read: rows j in [1, A) that move
+  // read: the rows that move (and every accepted key when they are rotated)
   for (int it = tid; it < A * CPR * 2; it += 256) {
     const int kv = it / (A * CPR), rem = it % (A * CPR);
     const int j = rem / CPR, c = rem % CPR;
-    if (acc_s[j] == j) continue;
+    if (acc_s[j] == j && (kv || !p.rope)) continue;
     const int64_t off = compact_row(p, b, L + acc_s[j], h) * sizeof(T) + c * 16;
     stage[kv][j][c] = *reinterpret_cast<const uint4*>((kv ? vbase : kbase) + off);
   }
@@ -255,9 +257,35 @@ __global__ void __launch_bounds__(256) tv_compact_kernel(CompactParams p) {
   for (int it = tid; it < A * CPR * 2; it += 256) {
     const int kv = it / (A * CPR), rem = it % (A * CPR);
     const int j = rem / CPR, c = rem % CPR;
+    if (!kv && p.rope) continue;  // rotated keys below
     if (acc_s[j] == j) continue;
     const int64_t off = compact_row(p, b, L + j, h) * sizeof(T) + c * 16;
     *reinterpret_cast<uint4*>((kv ? vbase : kbase) + off) = stage[kv][j][c];
+  }
+  if (p.rope) {
+    constexpr int HC = CPR / 2;
+    for (int it = tid; it < A * HC; it += 256) {
+      const int j = it / HC, c = it % HC;
+      T lo[E], hi[E];
+      const uint4 ulo = stage[0][j][c], uhi = stage[0][j][c + HC];
+      __builtin_memcpy(lo, &ulo, 16);
+      __builtin_memcpy(hi, &uhi, 16);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        float cs, sn;
+        rope_cos_sin(L + j, c * E + e, D, p.rope_log2_theta, cs, sn);
+        float x = static_cast<float>(lo[e]), y = static_cast<float>(hi[e]);
+        rope_pair(x, y, cs, sn);
+        lo[e] = static_cast<T>(x);
+        hi[e] = static_cast<T>(y);
+      }
+      uint4 wlo, whi;
+      __builtin_memcpy(&wlo, lo, 16);
+      __builtin_memcpy(&whi, hi, 16);
+      char* row = kbase + compact_row(p, b, L + j, h) * sizeof(T);
+      *reinterpret_cast<uint4*>(row + c * 16) = wlo;
+      *reinterpret_cast<uint4*>(row + (c + HC) * 16) = whi;
+    }
   }
 }
 

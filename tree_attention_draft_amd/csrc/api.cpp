@@ -90,6 +90,8 @@ tv_status check_args(const tv_attn_args* a, bool pointers) {
     return fail(TV_ERR_INVALID_ARG, "max_prefix_len out of range");
   if (!(a->sm_scale >= 0.f) || !std::isfinite(a->sm_scale))
     return fail(TV_ERR_INVALID_ARG, "sm_scale must be finite and >= 0");
+  if (!(a->rope_theta >= 0.0) || !std::isfinite(a->rope_theta))
+    return fail(TV_ERR_INVALID_ARG, "rope_theta must be finite and >= 0");
   if (a->B == 0) return TV_OK;
   if (pointers && (!a->q || !a->k || !a->v || !a->parent || !a->prefix_len || !a->out))
     return fail(TV_ERR_INVALID_ARG, "null q, k, v, parent, prefix_len or out");
@@ -208,6 +210,8 @@ AttnParams make_params(const tv_attn_args* a, const Plan& pl) {
   p.rows_per_wg = pl.rows_per_wg;
   const float scale = a->sm_scale > 0.f ? a->sm_scale : 1.0f / std::sqrt((float)a->D);
   p.scale_log2 = scale * 1.4426950408889634f;
+  p.rope = a->rope_theta > 0.0;
+  p.rope_log2_theta = p.rope ? std::log2(a->rope_theta) : 0.0;
   if (pl.splits > 1) {
     p.ws_o = static_cast<float*>(a->workspace);
     p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + pl.ws_o_bytes);
@@ -317,6 +321,8 @@ tv_status check_compact(const tv_compact_args* a) {
     return fail(TV_ERR_INVALID_ARG, "bad kv_layout");
   if (a->max_prefix_len < 0 || a->max_prefix_len > (1 << 30))
     return fail(TV_ERR_INVALID_ARG, "max_prefix_len out of range");
+  if (!(a->rope_theta >= 0.0) || !std::isfinite(a->rope_theta))
+    return fail(TV_ERR_INVALID_ARG, "rope_theta must be finite and >= 0");
   if (a->B == 0) return TV_OK;
   if (!a->k || !a->v || !a->prefix_len || !a->parent || !a->accepted || !a->num_accepted)
     return fail(TV_ERR_INVALID_ARG, "null pointer argument");
@@ -399,6 +405,8 @@ extern "C" tv_status tree_kv_compact(const tv_compact_args* a, hipStream_t strea
   p.num_accepted = a->num_accepted;
   p.new_len = a->new_len;
   p.status = a->status;
+  p.rope = a->rope_theta > 0.0;
+  p.rope_log2_theta = p.rope ? std::log2(a->rope_theta) : 0.0;
   const hipError_t e = launch_compact(p, stream);
   if (e != hipSuccess) return fail(TV_ERR_HIP, hipGetErrorString(e));
   return TV_OK;

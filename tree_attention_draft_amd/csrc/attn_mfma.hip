@@ -302,12 +302,70 @@ __device__ inline void wait_tiles(int n) {
   }
 }
 
+// Fused rotary embedding of the tree keys held by the window of tiles it .. it+WIN-1: every
+// K row of logical key t in [L, kend) is rotated in place in LDS at position
+// L + depth(t - L); feature m of row r sits in chunk m/8 of the swizzled row, its partner
+// m + D/2 in chunk m/8 + CH/2.  Called by every thread of the workgroup between the
+// window's publishing barrier and a second barrier; V rows are untouched.  One pair per
+// step and no unrolling, so the few registers it needs fit beside the loop's live state.
+template <class C, int KT, int NST, int WIN>
+__device__ inline void rope_tree_keys(char* smem, int it, int ntiles, int kbeg, int kend,
+                                      int L, const uint64_t* mask_s, double log2_theta,
+                                      int tid, int nthreads) {
+  constexpr int H = C::CH * 4;  // D / 2 pairs per row
+  constexpr int D = 2 * H;
+  const int t_lo = max(L, kbeg + it * KT);
+  const int t_hi = min(kend, kbeg + min(it + WIN, ntiles) * KT);
+#pragma unroll 1
+  for (int item = tid; item < (t_hi - t_lo) * H; item += nthreads) {
+    const int t = t_lo + item / H;
+    const int mm = item % H;
+    const int tt = (t - kbeg) / KT;
+    const int r = (t - kbeg) % KT;
+    float cs, sn;
+    rope_cos_sin(L + depth_of(mask_s[t - L]), mm, D, log2_theta, cs, sn);
+    char* row = smem + (tt % NST) * C::STAGEB + r * C::ROWB + (mm % 8) * 2;
+    __bf16* px = reinterpret_cast<__bf16*>(row + (((mm / 8) ^ swz_k<C::CH>(r)) << 4));
+    __bf16* py = reinterpret_cast<__bf16*>(row + (((mm / 8 + C::CH / 2) ^ swz_k<C::CH>(r)) << 4));
+    float x = static_cast<float>(*px), y = static_cast<float>(*py);
+    rope_pair(x, y, cs, sn);
+    *px = static_cast<__bf16>(x);
+    *py = static_cast<__bf16>(y);
+  }
+}
+
+// Fused rotary embedding of one wave's Q operand registers of tile t (node at position
+// pos): the lane parks its DS operands in a private LDS slot, rotates them there with a
+// plain loop (register arrays take static indices only) and reloads them.  Feature
+// m = 32s + 8lh + e sits in operand s, element e; its partner m + D/2 in operand s + DS/2.
+template <int D>
+__device__ inline void rope_q_tile(bf16x8 (&q)[D / 32], char* slot, int pos, int lh,
+                                   double log2_theta) {
+  constexpr int DS = D / 32;
+#pragma unroll
+  for (int s = 0; s < DS; ++s) *reinterpret_cast<bf16x8*>(slot + 16 * 64 * s) = q[s];
+#pragma unroll 1
+  for (int i = 0; i < DS / 2 * 8; ++i) {
+    const int s = i / 8, e = i % 8;
+    float cs, sn;
+    rope_cos_sin(pos, 32 * s + 8 * lh + e, D, log2_theta, cs, sn);
+    __bf16* px = reinterpret_cast<__bf16*>(slot + 16 * 64 * s) + e;
+    __bf16* py = reinterpret_cast<__bf16*>(slot + 16 * 64 * (s + DS / 2)) + e;
+    float x = static_cast<float>(*px), y = static_cast<float>(*py);
+    rope_pair(x, y, cs, sn);
+    *px = static_cast<__bf16>(x);
+    *py = static_cast<__bf16>(y);
+  }
+#pragma unroll
+  for (int s = 0; s < DS; ++s) q[s] = *reinterpret_cast<const bf16x8*>(slot + 16 * 64 * s);
+}
+
 // TN full 16-node tiles per wave (wave w = query head w of the group).  RR = 1 adds the
 // shared remainder tile: the N - 16*TN nodes past the full tiles, packed node-major
 // across the g heads (row = (node - 16*TN) * g + head), computed by wave it % NW on key
 // tile `it`; each wave keeps its own online-softmax partial of that tile and the partials
 // are merged through LDS at the end (the same maths as the split merge).
-template <int D, int KT, int NST, int TN, int RR, int NW>
+template <int D, int KT, int NST, int TN, int RR, int NW, bool ROPE>
 __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) {
   using C = MfmaCfg<D, KT, NST, TN, NW>;
   constexpr int DS = C::DS, DB = C::DB, KB = C::KB, KS = C::KS;
@@ -395,6 +453,17 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
   }
   wait_vmcnt<0>();
   __syncthreads();  // mask_s and pt_s visible
+
+  if constexpr (ROPE) {
+    // ---- fused rotary embedding of the queries, node i at L + depth(i), in lane-private
+    // LDS slots of the (still idle) ring: DS KB per wave ----
+    static_assert(NW * DS * 1024 <= NST * C::STAGEB, "query slots fit the ring");
+    char* slot = smem + w * DS * 1024 + 16 * lane;
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+      rope_q_tile<D>(qreg[t], slot, L + depth_of(mask_s[node_of[t]]), lh, p.rope_log2_theta);
+    __syncthreads();  // the ring may now be overwritten
+  }
 
   // ---- start the first two windows streaming ----
   const LoadPlan<C, NW> lp(p, w, lane);
@@ -527,6 +596,11 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
                                 kbeg + tn * KT, kend, fast, w, lane);
       }
     }
+    if (ROPE && kbeg + (it + WIN) * KT > L) {  // the window holds tree keys (uniform)
+      rope_tree_keys<C, KT, NST, WIN>(smem, it, ntiles, kbeg, kend, L, mask_s,
+                                      p.rope_log2_theta, tid, NW * 64);
+      __syncthreads();
+    }
     if (!head_on) continue;  // surplus wave of a group smaller than NW: loads only
 #pragma unroll
     for (int s = 0; s < WIN; ++s) {
@@ -607,13 +681,13 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
 constexpr int kMfmaKT = 32;
 constexpr int kMfmaNST = 4;
 
-template <int D>
+template <int D, bool ROPE>
 static hipError_t launch_d(const AttnParams& p, MfmaShape sh, hipStream_t s) {
   dim3 grid(p.num_splits, p.Hkv * p.row_chunks, p.B);
 #define TV_CASE(TN, RR, NW)                                                               \
   if (sh.tpw == TN && sh.rr == RR && sh.nw == NW) {                                       \
-    hipLaunchKernelGGL((tv_attn_mfma_kernel<D, kMfmaKT, kMfmaNST, TN, RR, NW>), grid,     \
-                       dim3(NW * 64), 0, s, p);                                           \
+    hipLaunchKernelGGL((tv_attn_mfma_kernel<D, kMfmaKT, kMfmaNST, TN, RR, NW, ROPE>),     \
+                       grid, dim3(NW * 64), 0, s, p);                                     \
     return hipGetLastError();                                                             \
   }
   TV_CASE(1, 0, 1) TV_CASE(1, 0, 2) TV_CASE(1, 0, 4) TV_CASE(1, 0, 8)
@@ -626,7 +700,8 @@ static hipError_t launch_d(const AttnParams& p, MfmaShape sh, hipStream_t s) {
 }
 
 hipError_t launch_attn_mfma(const AttnParams& p, int D, MfmaShape shape, hipStream_t s) {
-  return D == 64 ? launch_d<64>(p, shape, s) : launch_d<128>(p, shape, s);
+  if (p.rope) return D == 64 ? launch_d<64, true>(p, shape, s) : launch_d<128, true>(p, shape, s);
+  return D == 64 ? launch_d<64, false>(p, shape, s) : launch_d<128, false>(p, shape, s);
 }
 
 }  // namespace tv

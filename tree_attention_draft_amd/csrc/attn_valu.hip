@@ -74,6 +74,17 @@ __global__ void __launch_bounds__(256) tv_attn_valu_kernel(AttnParams p) {
     Qs[r][d] = val;
   }
   __syncthreads();
+  if (p.rope) {  // fused rotary embedding of the queries at L + depth (uniform branch)
+    for (int idx = tid; idx < ROWS * (D / 2); idx += 256) {
+      const int r = idx / (D / 2), mm = idx - (idx / (D / 2)) * (D / 2);
+      const int row = rc * ROWS + r;
+      if (row >= p.R) continue;
+      float cs, sn;
+      rope_cos_sin(L + depth_of(mask_s[row / p.g]), mm, D, p.rope_log2_theta, cs, sn);
+      rope_pair(Qs[r][mm], Qs[r][mm + D / 2], cs, sn);
+    }
+    __syncthreads();
+  }
 
   float m[RPW], l[RPW], o[RPW][E];
   uint64_t rmask[RPW];
@@ -103,6 +114,17 @@ __global__ void __launch_bounds__(256) tv_attn_valu_kernel(AttnParams p) {
       Vs[key][d] = vv;
     }
     __syncthreads();
+    if (p.rope && kt0 + KT > L) {  // tile holds tree keys: rotate them at L + depth
+      for (int idx = tid; idx < KT * (D / 2); idx += 256) {
+        const int key = idx / (D / 2), mm = idx - (idx / (D / 2)) * (D / 2);
+        const int t = kt0 + key;
+        if (t < L || t >= kend) continue;
+        float cs, sn;
+        rope_cos_sin(L + depth_of(mask_s[t - L]), mm, D, p.rope_log2_theta, cs, sn);
+        rope_pair(Ks[key][mm], Ks[key][mm + D / 2], cs, sn);
+      }
+      __syncthreads();
+    }
     const int t = kt0 + lane;
     const bool in_range = t < kend;
 #pragma unroll

@@ -85,6 +85,28 @@ __device__ inline uint64_t tile_allowed(uint64_t anc, int kt0, int L) {
   return prefix | tree;
 }
 
+// Rotary embedding, rotate-half form ("Tree attention mask for draft-tree verification",
+// "What interviewers probe next": a tree node is rotated at L + its depth): features m and
+// m + D/2 (m < D/2) turn by angle pos * theta^(-2m/D).  The angle is formed and reduced
+// to [-pi, pi] in fp64 so that long positions keep full fp32 accuracy in cos and sin.
+__device__ inline void rope_cos_sin(int pos, int m, int D, double log2_theta, float& c,
+                                    float& s) {
+  const double inv = exp2(-(2.0 * m / D) * log2_theta);
+  const double a = static_cast<double>(pos) * inv;
+  const double r = a - rint(a * 0.15915494309189535) * 6.283185307179586;
+  sincosf(static_cast<float>(r), &s, &c);
+}
+
+// (x, y) = (x cos - y sin, y cos + x sin): the pair (m, m + D/2) at one angle.
+__device__ inline void rope_pair(float& x, float& y, float c, float s) {
+  const float x0 = x;
+  x = x0 * c - y * s;
+  y = y * c + x0 * s;
+}
+
+// Depth of a node from its ancestor-or-self bitmask.
+__device__ inline int depth_of(uint64_t anc) { return __popcll(anc) - 1; }
+
 __device__ inline float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));

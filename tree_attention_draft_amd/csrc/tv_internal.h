@@ -42,6 +42,8 @@ struct AttnParams {
   int32_t node_chunks; // MFMA: workgroups splitting each head's 16-node tiles
   int32_t rows_per_wg; // packed rows one workgroup covers
   float scale_log2;    // sm_scale * log2(e)
+  int32_t rope;        // fused rotary embedding of q and the tree keys at L + depth
+  double rope_log2_theta;
 };
 
 // MFMA kernel shape: `nw` waves per workgroup, one query head each; every wave owns
@@ -87,6 +89,8 @@ struct CompactParams {
   const int32_t* num_accepted;
   int32_t* new_len;
   int32_t* status;
+  bool rope;             // write accepted keys rotated at L + j
+  double rope_log2_theta;
 };
 
 hipError_t launch_argmax(const AcceptParams& p, hipStream_t s);
