@@ -218,7 +218,9 @@ tv_status tree_verify_attn(const tv_attn_args* a, hipStream_t stream);
  *                         token), then -1.
  *   num_accepted [B]      A = number of accepted nodes = number of emitted tokens, 1..depth+1.
  *   workspace             device scratch of at least tree_accept_greedy_workspace_size()
- *                         bytes, 16-byte aligned (per-row partial maxima); caller-owned.
+ *                         = B * N * ceil(V / 8192) * 8 bytes, 16-byte aligned (one key per
+ *                         8192-entry slice of every row); caller-owned, contents need no
+ *                         initialisation.
  */
 typedef struct {
   tv_dtype dtype;
@@ -247,10 +249,10 @@ size_t tree_accept_greedy_workspace_size(const tv_accept_args* a);
  * walk from the root: at the current node the greedy token is emitted and the first child
  * (in node order) whose draft token equals it is accepted and becomes the current node;
  * the walk stops when no child matches (correction) or at a leaf (bonus).  Enqueues, on
- * `stream`, a kernel clearing the per-row partial maxima in the workspace, the argmax
- * kernel (workgroups over 16K-element slices of every row, HBM-bound on the logits, each
- * folding its best (value, index) into the row's partial with one 64-bit atomic max) and
- * the walk kernel (one workgroup per request).  Errors: TV_ERR_INVALID_ARG (null
+ * `stream`, the argmax kernel (one workgroup per 8192-entry slice of every row, HBM-bound on
+ * the logits, each storing its best (value, index) as an order-preserving 64-bit key in the
+ * workspace) and the walk kernel (one workgroup per request; it takes each row's largest
+ * slice key).  Errors: TV_ERR_INVALID_ARG (null
  * pointers, sizes, strides < V for lg_sn, misaligned logits for the given dtype),
  * TV_ERR_WORKSPACE, TV_ERR_HIP.  B == 0 is a no-op.
  */

@@ -265,6 +265,11 @@ def test_accept_workspace_checks(kw, status):
     L = tv.lib()
     assert L.tree_accept_greedy(ctypes.byref(a), None) == status
     assert L.tree_accept_greedy_workspace_size(ctypes.byref(base_accept_args())) == 2 * 10 * 8
+    # one key per 8192-entry slice of every row
+    big = base_accept_args(V=128256, lg_sn=128256, lg_sb=10 * 128256)
+    assert L.tree_accept_greedy_workspace_size(ctypes.byref(big)) == 2 * 10 * 16 * 8
+    big.workspace_bytes = 2 * 10 * 16 * 8 - 1
+    assert L.tree_accept_greedy(ctypes.byref(big), None) == 6
 
 
 def test_accept_empty_batch_is_noop():

@@ -54,6 +54,12 @@ def test_argmax_and_walk_bit_exact(dtype, V):
             r[V // 2] = r.max()
     x[1, 3, :] = 0.25
     x[1, 4, :] = -np.inf
+    if V > 9:              # zero is the max, -0 comes first: equal values, lowest index wins
+        x[0, 2, :] = -1.0
+        x[0, 2, 5] = -0.0
+        x[0, 2, 9] = 0.0
+        x[0, 3, :] = -2.0  # max only in the last element
+        x[0, 3, V - 1] = 1.0
     if V > 3:
         x[2, 7, 2] = np.nan            # first NaN wins
         x[2, 7, V - 1] = np.nan

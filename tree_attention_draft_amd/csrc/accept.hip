@@ -58,72 +58,95 @@ __device__ inline uint64_t arg_key(float v, int i) {
   return ((uint64_t)k << 32) | (uint32_t)(~(uint32_t)i);
 }
 
-constexpr int kArgSlice = 16384;  // elements of a row per workgroup
+constexpr int kArgUnroll = 4;  // 16-byte loads in flight per thread
 
-// Clears the per-row partial maxima (a kernel rather than a memset, so the sequence stays
-// safe to capture and replay in a graph).
-__global__ void tv_argmax_init_kernel(uint64_t* __restrict__ part, int rows) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < rows) part[i] = 0ull;
-}
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-// Workgroup (slice, row): 256 threads scan kArgSlice elements of one row with 16-byte
-// loads when the row is aligned for them (`vec`), element loads otherwise; a vector can
-// change a thread's candidate only if its max beats the current best or it holds a NaN
-// (its sum is then NaN too; an inf - inf sum only sends it down the exact path
-// needlessly).  Thread candidates reduce over the wave with shuffles and over the 4 waves
-// through LDS; lane 0 folds the result into the row's partial with one atomic max.
+// Workgroup (slice, row): 256 threads scan kArgSlice elements of one row.  With 16-byte
+// loads (`vec`: the row is aligned for them) a thread keeps only the running maximum of
+// its vectors and the index of the first vector that reached it (a vector replaces it only
+// when its own maximum is strictly greater, so among equal values the earliest vector
+// stays), plus a running maximum of the magnitude bits that reveals a NaN; the winning
+// element is located at the end by reading that one vector again, and a thread that saw a
+// NaN looks up its first NaN instead (rare).  Element loads cover unaligned rows and the
+// tail.  Thread candidates reduce over the wave with shuffles and over the 4 waves through
+// LDS; lane 0 stores the slice's key in the row's slot for this slice (every slot is
+// written, so the workspace needs no clearing).
 template <typename T>
 __global__ void __launch_bounds__(256) tv_argmax_kernel(const T* __restrict__ logits,
                                                         int64_t sb, int64_t sn, int N, int V,
                                                         uint64_t* __restrict__ part, bool vec) {
+  constexpr bool BF = sizeof(T) == 2;
   constexpr int E = 16 / sizeof(T);  // elements per 16-byte load
   const int row = blockIdx.y;
   const int b = row / N, n = row % N;
   const T* x = logits + (int64_t)b * sb + (int64_t)n * sn;
   const int lo = blockIdx.x * kArgSlice;
   const int hi = min(V, lo + kArgSlice);
-  ArgBest best{-INFINITY, 0x7fffffff};
-  bool any = false;
+  ArgBest best{-INFINITY, 0x7fffffff};  // "none yet": loses to every real candidate
   const int tid = threadIdx.x;
   int done = lo;
   if (vec) {
     const int v0 = lo / E, v1 = hi / E;  // lo is a multiple of E
     const uint4* xv = reinterpret_cast<const uint4*>(x);
-    constexpr int U = 4;
-    for (int k0 = v0 + tid; k0 < v1; k0 += 256 * U) {
-      uint4 w[U];
+    float run = -INFINITY;
+    int runk = -1;
+    uint32_t mag = 0;  // bf16: two 16-bit lanes; f32: one 32-bit lane
+    for (int k0 = v0 + tid; k0 < v1; k0 += 256 * kArgUnroll) {
+      uint4 w[kArgUnroll];
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+      for (int u = 0; u < kArgUnroll; ++u)
         if (k0 + 256 * u < v1) w[u] = xv[k0 + 256 * u];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < kArgUnroll; ++u) {
         const int k = k0 + 256 * u;
         if (k >= v1) break;
-        const T* e = reinterpret_cast<const T*>(&w[u]);
-        float mx = static_cast<float>(e[0]), sm = mx;
+        const uint32_t d[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+        float m = -INFINITY;
 #pragma unroll
-        for (int t = 1; t < E; ++t) {
-          const float f = static_cast<float>(e[t]);
-          mx = fmaxf(mx, f);
-          sm += f;
+        for (int q = 0; q < 4; ++q) {
+          if constexpr (BF) {
+            m = fmaxf(m, fmaxf(__uint_as_float(d[q] << 16), __uint_as_float(d[q] & 0xffff0000u)));
+            mag = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(
+                      __builtin_bit_cast(u16x2, mag), __builtin_bit_cast(u16x2, d[q] & 0x7fff7fffu)));
+          } else {
+            m = fmaxf(m, __uint_as_float(d[q]));
+            mag = max(mag, d[q] & 0x7fffffffu);
+          }
         }
-        if (!any || mx > best.v || sm != sm) {
-#pragma unroll
-          for (int t = 0; t < E; ++t) {
-            const ArgBest c{static_cast<float>(e[t]), k * E + t};
-            if (!any || better(c, best)) best = c;
-            any = true;
+        if (m > run || runk < 0) {
+          run = m;
+          runk = k;
+        }
+      }
+    }
+    const bool nan = BF ? ((mag & 0xffffu) > 0x7f80u || (mag >> 16) > 0x7f80u) : mag > 0x7f800000u;
+    if (nan) {  // rare: the candidate is this thread's first NaN
+      for (int k = v0 + tid; k < v1 && best.i == 0x7fffffff; k += 256) {
+        const uint4 wv = xv[k];
+        const T* e = reinterpret_cast<const T*>(&wv);
+        for (int t = 0; t < E; ++t) {
+          const float f = static_cast<float>(e[t]);
+          if (f != f) {
+            best = ArgBest{f, k * E + t};
+            break;
           }
         }
       }
+    } else if (runk >= 0) {  // the first element of the winning vector that equals its max
+      const uint4 wv = xv[runk];
+      const T* e = reinterpret_cast<const T*>(&wv);
+      int t = E - 1;
+#pragma unroll
+      for (int q = E - 1; q >= 0; --q)
+        if (static_cast<float>(e[q]) == run) t = q;
+      best = ArgBest{run, runk * E + t};
     }
     done = v1 * E;
   }
   for (int k = done + tid; k < hi; k += 256) {
     const ArgBest c{load_f(x + k), k};
-    if (!any || better(c, best)) best = c;
-    any = true;
+    if (better(c, best)) best = c;
   }
   best = wave_best(best);
   __shared__ float sv[4];
@@ -140,16 +163,15 @@ __global__ void __launch_bounds__(256) tv_argmax_kernel(const T* __restrict__ lo
       const ArgBest c{sv[k], si[k]};
       if (better(c, r)) r = c;
     }
-    if (r.i < hi) atomicMax(reinterpret_cast<unsigned long long*>(part + row),
-                            (unsigned long long)arg_key(r.v, r.i));
+    part[(int64_t)row * gridDim.x + blockIdx.x] = r.i < hi ? arg_key(r.v, r.i) : 0ull;
   }
 }
 
-// One workgroup per request: the tree, the draft tokens and the greedy tokens are staged
-// in LDS by N lanes, then lane 0 walks.  Children of a node have larger indices
+// One workgroup per request: the tree, the draft tokens and the greedy tokens (the maximum
+// of each row's S slice keys) are staged in LDS by N lanes, then lane 0 walks.  Children of a node have larger indices
 // (parent-before-child order), so each step moves strictly forward and the walk ends
 // within N steps whatever the parent array holds.
-__global__ void __launch_bounds__(64) tv_walk_kernel(int B, int N,
+__global__ void __launch_bounds__(64) tv_walk_kernel(int B, int N, int S,
                                                      const int32_t* __restrict__ tokens,
                                                      int tokens_sb,
                                                      const int32_t* __restrict__ parent,
@@ -167,8 +189,11 @@ __global__ void __launch_bounds__(64) tv_walk_kernel(int B, int N,
   if (tid < N) {
     par[tid] = parent[(int64_t)b * parent_sb + tid];
     tok[tid] = tokens[(int64_t)b * tokens_sb + tid];
-    // the row's argmax index is the complement of the low word of its partial
-    tg[tid] = (int32_t)~(uint32_t)(part[(int64_t)b * N + tid] & 0xffffffffull);
+    // the row's argmax index is the complement of the low word of its largest slice key
+    const uint64_t* slots = part + ((int64_t)b * N + tid) * S;
+    uint64_t key = slots[0];
+    for (int j = 1; j < S; ++j) key = max(key, slots[j]);
+    tg[tid] = (int32_t)~(uint32_t)(key & 0xffffffffull);
     target[(int64_t)b * N + tid] = tg[tid];
     acc[tid] = -1;
     em[tid] = -1;
@@ -291,12 +316,9 @@ __global__ void __launch_bounds__(256) tv_compact_kernel(CompactParams p) {
 
 hipError_t launch_argmax(const AcceptParams& p, hipStream_t s) {
   const int rows = p.B * p.N;
+  const int S = (p.V + kArgSlice - 1) / kArgSlice;
   uint64_t* part = static_cast<uint64_t*>(p.workspace);
-  hipLaunchKernelGGL(tv_argmax_init_kernel, dim3((rows + 255) / 256), dim3(256), 0, s, part,
-                     rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const dim3 grid((p.V + kArgSlice - 1) / kArgSlice, rows);
+  const dim3 grid(S, rows);
   if (p.bf16)
     hipLaunchKernelGGL(tv_argmax_kernel<__bf16>, grid, dim3(256), 0, s,
                        static_cast<const __bf16*>(p.logits), p.lg_sb, p.lg_sn, p.N, p.V, part,
@@ -305,9 +327,9 @@ hipError_t launch_argmax(const AcceptParams& p, hipStream_t s) {
     hipLaunchKernelGGL(tv_argmax_kernel<float>, grid, dim3(256), 0, s,
                        static_cast<const float*>(p.logits), p.lg_sb, p.lg_sn, p.N, p.V, part,
                        p.vec);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(tv_walk_kernel, dim3(p.B), dim3(64), 0, s, p.B, p.N, p.tokens,
+  hipLaunchKernelGGL(tv_walk_kernel, dim3(p.B), dim3(64), 0, s, p.B, p.N, S, p.tokens,
                      p.tokens_sb, p.parent, p.parent_sb, part, p.target, p.accepted, p.emitted,
                      p.num_accepted);
   return hipGetLastError();

@@ -303,7 +303,7 @@ tv_status check_accept(const tv_accept_args* a) {
     return fail(TV_ERR_INVALID_ARG, "logits not aligned to its element size");
   if (a->V > (1 << 30)) return fail(TV_ERR_INVALID_ARG, "V > 2^30");
   if ((int64_t)a->B * a->N > 65535) return fail(TV_ERR_UNSUPPORTED, "B * N > 65535");
-  const size_t need = (size_t)a->B * a->N * 8;
+  const size_t need = tree_accept_greedy_workspace_size(a);
   if (!a->workspace || a->workspace_bytes < need)
     return fail(TV_ERR_WORKSPACE, "workspace missing or smaller than required");
   if (!aligned16(a->workspace)) return fail(TV_ERR_INVALID_ARG, "workspace not 16-byte aligned");
@@ -413,8 +413,9 @@ extern "C" tv_status tree_kv_compact(const tv_compact_args* a, hipStream_t strea
 }
 
 extern "C" size_t tree_accept_greedy_workspace_size(const tv_accept_args* a) {
-  if (!a || a->B < 0 || a->N < 1 || a->N > TV_MAX_NODES) return 0;
-  return (size_t)a->B * a->N * 8;
+  if (!a || a->B < 0 || a->N < 1 || a->N > TV_MAX_NODES || a->V < 1) return 0;
+  const size_t slices = ((size_t)a->V + tv::kArgSlice - 1) / tv::kArgSlice;
+  return (size_t)a->B * a->N * slices * 8;
 }
 
 extern "C" size_t tv_accept_args_sizeof(void) { return sizeof(tv_accept_args); }

@@ -13,6 +13,7 @@ tv_status fail(tv_status s, const char* detail);
 
 constexpr int kKeysPerTile = 64;  // split chunks are multiples of this many keys
 constexpr int kMaxPageSlice = 1024;  // page-table entries one MFMA workgroup stages in LDS
+constexpr int kArgSlice = 8192;      // logits of a row per argmax workgroup (one key slot each)
 
 // Everything a kernel needs, passed by value.  Strides in elements.
 struct AttnParams {
@@ -69,7 +70,7 @@ struct AcceptParams {
   int32_t* accepted;
   int32_t* emitted;
   int32_t* num_accepted;
-  void* workspace;  // B*N uint64 per-row partial maxima
+  void* workspace;  // B*N*ceil(V/kArgSlice) uint64 slice keys
 };
 
 // Device-side arguments of the KV compaction kernel.
