@@ -217,6 +217,24 @@ def test_relabelling_permutes_outputs():
         assert np.abs(out2[b] - out1[b][perm]).max() <= 2e-2
 
 
+def test_rising_scores_take_the_overflow_fallback():
+    # Every query is the same +-1 vector u and prefix key t is u * t/64, so the scores grow
+    # by about 0.14 log2 units per key at this scale: far past the 64-unit weight bound
+    # several times per request, which the fast softmax step must catch and rebase.
+    paths, _ = random_trees(1900, 2, 33, 8)
+    c = Case("rising_scores", [1024, 700], trees=paths, seed=1900)
+    rng = np.random.Generator(np.random.PCG64(1901))
+    u = np.where(rng.random(128) < 0.5, -1.0, 1.0).astype(np.float32)
+    c.host["q"][:] = workloads.f32_to_bf16_bits(np.broadcast_to(u, c.host["q"].shape).copy(),
+                                                finite=True)
+    for b, L in enumerate(c.L):
+        ramp = (np.arange(L, dtype=np.float32) / 64.0)[:, None, None] * u
+        c.host["k"][b, :L] = workloads.f32_to_bf16_bits(
+            np.broadcast_to(ramp, (L, c.Hkv, 128)).copy(), finite=True)
+    out, lse = c.run(sm_scale=0.05)
+    c.check(out, lse)
+
+
 def test_shared_tree_strided_tensors_and_no_lse():
     par = ometa.build_from_paths(TEN, 0)["parent"]
     c = Case("shared_strided", [300, 301, 302], parents=[par] * 3, seed=1800)

@@ -54,9 +54,11 @@ __device__ inline void wait_vmcnt() {
 // cannot tell which LDS bytes such a copy writes, so when it sees one it drains every
 // outstanding load (vmcnt 0) before each barrier and LDS read, which would serialise the
 // ring.  Completion is tracked explicitly with wait_vmcnt instead.  M0 carries the LDS
-// address; the compiler sets M0 itself before any of its own uses.
+// address; the compiler sets M0 itself before any of its own uses.  The loads carry the
+// non-temporal hint (nt): every K/V byte is read exactly once, and streaming it past the
+// caches raises the sustained HBM read rate of this access pattern by about 13% on MI355X.
 __device__ inline void lds_load16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt"
                :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(g) : "memory", "m0");
 }
 
@@ -69,13 +71,14 @@ __device__ inline void lds_load16_s(const void* base, uint32_t voff, uint32_t ld
   const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane((uint32_t)a));
   const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)));
   const uint64_t sa = (static_cast<uint64_t>(hi) << 32) | static_cast<uint64_t>(lo);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
                :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(sa)
                : "memory", "m0");
 }
 
-// Online-softmax rebasing threshold in log2 units (see the softmax step of the kernel).
+// Online-softmax thresholds in log2 units (see the softmax helpers below).
 constexpr float kRebase = 8.f;
+constexpr float kTripSum = 0x1p64f;  // per-lane sum of a fast step's weights
 
 template <int D, int KT, int NST, int TN, int NW>
 struct MfmaCfg {
@@ -187,77 +190,78 @@ __device__ inline void issue_tile(const AttnParams& p, const RowMap& rm,
 }
 
 // Online softmax of one 16-row x KT-key score tile held transposed (lane: 4 keys of one
-// row per 16-key block), with lazy rebasing: a row keeps its reference max m until one of
-// its scores exceeds it by more than kRebase (log2 units).  Per-row state kept per lane:
-//   m    reference max in scaled log2 units (-inf before the first finite score)
-//   nm   -m, or 0 while m is -inf: the addend of the exponent
-//   thr  (m + kRebase) / c: the rebase test in raw score units (c > 0)
-//   l    this lane's share of the row sum, in units of 2^m
-// Each lane tests only its own raw scores against thr; the row max over lanes and the
-// O/l rescale run only when some lane trips the test, which after the first tile is
-// rare.  Exponents stay <= kRebase, so P <= 2^kRebase (no overflow in fp32 or bf16) and
-// the final division by l cancels the reference.
+// row per 16-key block).  The row's reference max m (scaled log2 units) enters the matrix
+// core as the initial value of the Q.K^T accumulator, -m/c in raw score units, so the
+// scores come back as S = s - m/c and the weights are 2^(c*S), c = sm_scale * log2(e) > 0.
+// Per-row state kept per lane:
+//   m    reference max (-inf before the row has seen an allowed key)
+//   nm4  -m/c (0 while m is -inf) in four copies: the accumulator's initial value
+//   l    this lane's share of the row sum of the weights, in units of 2^m
+//   o    the output accumulator, in units of 2^m
+// Exact step (a row's first key tile, and every tile that reaches the tree tail): the row
+// max decides; a row that has no reference yet, or whose max exceeds the reference by more
+// than kRebase, moves its reference to that max and rescales o and l.  Fast step (every
+// other tile): the weights are formed against the current reference with no max at all,
+// and only their per-lane sum is tested; a sum above kTripSum (or not finite) sends the
+// tile back through the exact step before its weights are used.  Either way every weight
+// is at most 2^64, so weights, row sums and outputs stay finite, and the final division by
+// l cancels the reference: the result is exact up to rounding.
 
-// Masks the tile (masked tiles only) and returns this lane's raw max.  `allow` holds this
-// lane's allowed-key bits: bit 16*kb + i.
+// Masked scores of the tree tail: `allow` holds this lane's allowed-key bits, bit 16*kb + i.
 template <int KB>
-__device__ inline float mask_and_max(f32x4 (&sacc)[KB], bool masked, uint64_t allow) {
-  if (masked) {
+__device__ inline void apply_mask(f32x4 (&sacc)[KB], uint64_t allow) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+  for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        sacc[kb][i] = ((allow >> (16 * kb + i)) & 1ull) ? sacc[kb][i] : -INFINITY;
-  }
+    for (int i = 0; i < 4; ++i)
+      sacc[kb][i] = ((allow >> (16 * kb + i)) & 1ull) ? sacc[kb][i] : -INFINITY;
+}
+
+// Exact step of one row tile (see above); moves S to the new reference in place.
+template <int KB, int DB>
+__device__ inline void rebase_exact(f32x4 (&sacc)[KB], float c, float& m, f32x4& nm4,
+                                    float& l, f32x4 (&o)[DB]) {
   float mx = sacc[0][0];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
     for (int i = (kb == 0 ? 1 : 0); i < 4; ++i) mx = fmaxf(mx, sacc[kb][i]);
-  return mx;
-}
-
-// Rare path: move the row's reference to its current max and rescale what was summed.
-template <int DB>
-__device__ inline void rebase_row(float mx_raw, float c, float& m, float& nm, float& thr,
-                                  float& l, f32x4 (&o)[DB]) {
-  float mx = mx_raw * c;
   mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(m, mx);
-  if (m_new != -INFINITY) {
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 when m was -inf
+  mx = fmaxf(mx, __shfl_xor(mx, 32));  // row max of S, raw units
+  const bool fresh = m == -INFINITY;
+  const bool need = fresh ? mx != -INFINITY : mx * c > kRebase;
+  if (__any(need)) {  // wave-uniform
+    const float shift = need ? mx : 0.f;
+    const float alpha = need ? (fresh ? 0.f : __builtin_amdgcn_exp2f(-mx * c)) : 1.f;
     l *= alpha;
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] *= alpha;
-    m = m_new;
-    nm = -m_new;
-    thr = (m_new + kRebase) / c;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) sacc[kb] -= shift;
+    nm4 -= shift;
+    if (need) m = fresh ? mx * c : m + mx * c;
   }
 }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// P = 2^(c*s - m) packed to bf16 as the B operand of P.V; the row sum accumulates the
-// same rounded values (dot with (1, 1)), so numerator and denominator use equal weights.
+// P = 2^(c*S) packed to bf16 as the B operand of P.V; returns this lane's sum of the same
+// rounded values (dot with (1, 1)), so numerator and denominator use equal weights.
 template <int KB, int KS>
-__device__ inline void exp_pack(const f32x4 (&sacc)[KB], float c, float nm, float& l,
-                                bf16x8 (&pk)[KS]) {
+__device__ inline float exp_pack(const f32x4 (&sacc)[KB], float c, bf16x8 (&pk)[KS]) {
+  const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+  float lt = 0.f;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      pk[kb >> 1][(kb & 1) * 4 + i] =
-          static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, nm)));
-  const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const bf16x2 pair = {pk[ks][2 * h], pk[ks][2 * h + 1]};
-      l = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, l, false);
+    for (int h = 0; h < 2; ++h) {
+      const bf16x2 pair = {static_cast<__bf16>(__builtin_amdgcn_exp2f(sacc[kb][2 * h] * c)),
+                           static_cast<__bf16>(__builtin_amdgcn_exp2f(sacc[kb][2 * h + 1] * c))};
+      pk[kb >> 1][(kb & 1) * 4 + 2 * h] = pair[0];
+      pk[kb >> 1][(kb & 1) * 4 + 2 * h + 1] = pair[1];
+      lt = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lt, false);
     }
-  }
+  return lt;
 }
 
 // Final store of one row: normalised output and natural-log LSE, or the split partial.
@@ -373,6 +377,9 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
   __shared__ __attribute__((aligned(1024))) char smem[NST * C::STAGEB];
   __shared__ uint64_t mask_s[TV_MAX_NODES];
   __shared__ int32_t pt_s[kMaxPageSlice];
+  // the shared remainder tile's query operands (B-operand layout, [k-step][lane]): read
+  // from LDS on the key tiles a wave computes it, so they take no registers in the loop
+  __shared__ bf16x8 qrem_s[RR ? DS * 64 : 1];
   static_assert(!RR || NW * 16 * D * 4 <= NST * C::STAGEB, "merge buffer fits the ring");
   static_assert(!RR || NW * 16 * 2 <= kMaxPageSlice, "merge (m, l) fits the page slice");
 
@@ -465,6 +472,16 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
     __syncthreads();  // the ring may now be overwritten
   }
 
+  // ---- park the remainder tile's query operands in LDS ----
+  const float c = p.scale_log2;
+  if constexpr (RR) {
+    if (w == 0) {
+#pragma unroll
+      for (int s = 0; s < DS; ++s) qrem_s[s * 64 + lane] = qreg[TN][s];
+    }
+    __syncthreads();  // qrem_s visible before the first remainder tile
+  }
+
   // ---- start the first two windows streaming ----
   const LoadPlan<C, NW> lp(p, w, lane);
   const bool fast = !p.paged && (int64_t)(KT - 1) * p.kv_st * 2 + 2 * D <= INT32_MAX;
@@ -475,17 +492,16 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
                             w, lane);
 
   f32x4 o[TT][DB];
-  float m[TT], l[TT], nm[TT], thr[TT];
+  f32x4 nm4[TT];
+  float m[TT], l[TT];
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
     m[t] = -INFINITY;
-    thr[t] = -INFINITY;
-    nm[t] = 0.f;
+    nm4[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     l[t] = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[t][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const float c = p.scale_log2;
 
   // One key tile: S^T = K Q^T, mask, online softmax, O^T += V^T P^T.
   auto tile = [&](int it, bool do_rem) {
@@ -494,6 +510,11 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
     const char* vs = ks + C::TILEB;
 
     // ---- S^T = K Q^T ----
+    bf16x8 qr[DS];
+    if (RR && do_rem) {
+#pragma unroll
+      for (int s = 0; s < DS; ++s) qr[s] = qrem_s[s * 64 + lane];
+    }
     f32x4 sacc[TT][KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -506,39 +527,49 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
 #pragma unroll
       for (int t = 0; t < TT; ++t) {
         if (t >= TN && !do_rem) continue;
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 acc = nm4[t];  // scores come back relative to the row's reference
 #pragma unroll
         for (int s = 0; s < DS; ++s)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s], qreg[t][s], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s], t < TN ? qreg[t][s] : qr[s], acc,
+                                                        0, 0, 0);
         sacc[t][kb] = acc;
       }
     }
 
-    // ---- tree-tail mask, lazy rebase test ----
+    // ---- weights: exact step on a row tile's first key tile and on the tree tail, fast
+    // step with the row-sum test elsewhere ----
     const bool masked = kt0 + KT > L;
-    float mx[TT];
+    bf16x8 pk[TT][KS];
+    float lt[TT];
     bool trip = false;
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
       if (t >= TN && !do_rem) continue;
-      const uint64_t allow = masked ? tile_allowed(mask_s[node_of[t]], kt0, L) >> (4 * lh) : 0ull;
-      mx[t] = mask_and_max<KB>(sacc[t], masked, allow);
-      trip |= mx[t] > thr[t];
+      // a full tile's first key tile is the split's first; the remainder tile's is the
+      // first this wave computes (it < NW)
+      const bool exact = masked || (t < TN ? it == 0 : it < NW);
+      if (exact) {
+        if (masked) apply_mask<KB>(sacc[t], tile_allowed(mask_s[node_of[t]], kt0, L) >> (4 * lh));
+        rebase_exact<KB, DB>(sacc[t], c, m[t], nm4[t], l[t], o[t]);
+      }
+      lt[t] = exp_pack<KB, KS>(sacc[t], c, pk[t]);
+      if (!exact) trip |= !(lt[t] <= kTripSum);
     }
-    if (__any(trip)) {  // wave-uniform, rare after the first tile
+    if (__any(trip)) {  // wave-uniform; never on ordinary data after a row's first tile
 #pragma unroll
       for (int t = 0; t < TT; ++t) {
         if (t >= TN && !do_rem) continue;
-        if (__any(mx[t] > thr[t])) rebase_row<DB>(mx[t], c, m[t], nm[t], thr[t], l[t], o[t]);
+        if (masked || (t < TN ? it == 0 : it < NW)) continue;
+        if (__any(!(lt[t] <= kTripSum))) {
+          rebase_exact<KB, DB>(sacc[t], c, m[t], nm4[t], l[t], o[t]);
+          lt[t] = exp_pack<KB, KS>(sacc[t], c, pk[t]);
+        }
       }
     }
-
-    // ---- P, row sums ----
-    bf16x8 pk[TT][KS];
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
       if (t >= TN && !do_rem) continue;
-      exp_pack<KB, KS>(sacc[t], c, nm[t], l[t], pk[t]);
+      l[t] += lt[t];
     }
 
     // ---- O^T += V^T P^T, V^T read transposed from V's row-major tile.  The operand of
