@@ -76,6 +76,19 @@ __device__ inline void lds_load16_s(const void* base, uint32_t voff, uint32_t ld
                : "memory", "m0");
 }
 
+// Wave issue priority around a block of matrix instructions: the two waves sharing a SIMD
+// mostly alternate between matrix and vector work; letting the wave that is issuing MFMAs
+// go first keeps the matrix pipe fed while the other fills the gaps with its vector work.
+// The scheduling barriers keep the compiler from moving instructions across the change.
+__device__ inline void mfma_priority(bool high) {
+  __builtin_amdgcn_sched_barrier(0);
+  if (high)
+    __builtin_amdgcn_s_setprio(1);
+  else
+    __builtin_amdgcn_s_setprio(0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Online-softmax thresholds in log2 units (see the softmax helpers below).
 constexpr float kRebase = 8.f;
 constexpr float kTripSum = 0x1p64f;  // per-lane sum of a fast step's weights
@@ -128,31 +141,40 @@ __device__ inline int64_t row_offset(const AttnParams& p, const RowMap& rm, int 
   return rm.head_off + (int64_t)rm.pt[pi - rm.pbase] * p.kv_sb + (int64_t)slot * p.kv_st;
 }
 
-// Per-wave load assignment: instruction ii of a tile copies 1 KB = RPI rows of K (first
-// half of the instructions) or V (second half) into the stage.  For each instruction a lane
-// owns one 16-byte chunk: row r, LDS position lane % CH, global chunk swizzled.
+// Per-wave load assignment.  When a wave has an even number LPW of 1 KB load instructions
+// per tile, its first LPW/2 copy K and the others V (known at compile time); K (V)
+// instruction jj of wave w covers rows (jj*NW + w)*RPI ... of its tile.  Otherwise
+// (LPW = 1) instruction i = w of the tile's LI copies K when i < LI/2, else V.  For each
+// instruction a lane owns one 16-byte chunk: row r, LDS position lane % CH, global chunk
+// swizzled.
 template <class C, int NW>
 struct LoadPlan {
-  bool is_v[C::LPW];      // wave-uniform
-  uint32_t dst[C::LPW];   // LDS byte offset within a stage (wave-uniform)
-  uint32_t off[C::LPW];   // contiguous KV: byte offset of the chunk from the tile's row 0
+  static constexpr bool kSplit = C::LPW % 2 == 0;
+  static constexpr int HALF = kSplit ? C::LPW / 2 : 1;
+  static_assert(kSplit || C::LPW == 1, "load instructions per wave");
+  bool v1;               // LPW = 1: this wave copies V (wave-uniform)
+  uint32_t dst0;         // LDS byte offset of the wave's first K (or only) instruction
+  uint32_t off[C::LPW];  // contiguous KV: byte offset of the chunk from the tile's row 0
 
+  __device__ inline bool is_v(int ii) const { return kSplit ? ii >= HALF : v1; }
   // row within the tile and byte offset of the (swizzled) global chunk within the row
-  static __device__ inline void chunk_of(int ii, int w, int lane, int& r, int& coff) {
-    const int i = ii * NW + w;
-    const bool v = i >= C::LI / 2;
-    const int ik = v ? i - C::LI / 2 : i;
+  __device__ inline void chunk_of(int ii, int w, int lane, int& r, int& coff) const {
+    const bool v = is_v(ii);
+    const int ik = kSplit ? (ii % HALF) * NW + w : (v ? w - C::LI / 2 : w);
     r = ik * C::RPI + lane / C::CH;
     coff = ((lane % C::CH) ^ (v ? swz_v<C::CH>(r) : swz_k<C::CH>(r))) * 16;
   }
+  // LDS byte offset of instruction ii within a stage
+  __device__ inline uint32_t dst(int ii) const {
+    if constexpr (kSplit) return dst0 + (ii >= HALF ? C::TILEB : 0) + (ii % HALF) * NW * 1024;
+    return dst0;
+  }
 
   __device__ LoadPlan(const AttnParams& p, int w, int lane) {
+    v1 = !kSplit && w >= C::LI / 2;
+    dst0 = kSplit ? w * 1024 : (v1 ? C::TILEB + (w - C::LI / 2) * 1024 : w * 1024);
 #pragma unroll
     for (int ii = 0; ii < C::LPW; ++ii) {
-      const int i = ii * NW + w;
-      is_v[ii] = i >= C::LI / 2;
-      const int ik = is_v[ii] ? i - C::LI / 2 : i;
-      dst[ii] = (is_v[ii] ? C::TILEB : 0) + ik * 1024;
       int r, coff;
       chunk_of(ii, w, lane, r, coff);
       off[ii] = (uint32_t)((int64_t)r * p.kv_st * 2 + coff);
@@ -176,16 +198,16 @@ __device__ inline void issue_tile(const AttnParams& p, const RowMap& rm,
     const char* vb = vg + row0;
 #pragma unroll
     for (int ii = 0; ii < C::LPW; ++ii)
-      lds_load16_s(lp.is_v[ii] ? vb : kb, lp.off[ii], stage + lp.dst[ii]);
+      lds_load16_s(lp.is_v(ii) ? vb : kb, lp.off[ii], stage + lp.dst(ii));
     return;
   }
 #pragma unroll
   for (int ii = 0; ii < C::LPW; ++ii) {
     int r, coff;
-    LoadPlan<C, NW>::chunk_of(ii, w, lane, r, coff);
+    lp.chunk_of(ii, w, lane, r, coff);
     const int t = min(kt0 + r, kend - 1);
-    const char* src = (lp.is_v[ii] ? vg : kg) + row_offset(p, rm, t) * 2 + coff;
-    lds_load16(src, stage + lp.dst[ii]);
+    const char* src = (lp.is_v(ii) ? vg : kg) + row_offset(p, rm, t) * 2 + coff;
+    lds_load16(src, stage + lp.dst(ii));
   }
 }
 
@@ -509,7 +531,8 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
     const char* ks = smem + (it % NST) * C::STAGEB;
     const char* vs = ks + C::TILEB;
 
-    // ---- S^T = K Q^T ----
+    // ---- S^T = K Q^T (raised issue priority: see mfma_priority) ----
+    mfma_priority(true);
     bf16x8 qr[DS];
     if (RR && do_rem) {
 #pragma unroll
@@ -536,6 +559,7 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
       }
     }
 
+    mfma_priority(false);
     // ---- weights: exact step on a row tile's first key tile and on the tree tail, fast
     // step with the row-sum test elsewhere ----
     const bool masked = kt0 + KT > L;
@@ -587,6 +611,7 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
           (TV_LDS v4i16*)(vs + r1 * C::ROWB + ((chunk ^ swz_v<C::CH>(r1)) << 4) + half));
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
+    mfma_priority(true);
     constexpr int NV = DB * KS;                  // V operands per tile, db-major
     constexpr int PF = 1;                        // operands in flight ahead of the MFMAs
     bf16x8 va[PF + 1];
@@ -603,6 +628,7 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
                                                            o[t][db], 0, 0, 0);
       }
     }
+    mfma_priority(false);
   };
 
   // Tiles go in windows of WIN = NST/2: one barrier per window publishes its WIN tiles and
