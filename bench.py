@@ -5,7 +5,8 @@ One step is the whole hot path for one batch: the host C++ builder turns every r
 candidate rank paths into parent/depth/bitmask/position arrays, the parent arrays are
 copied to the device, the device metadata kernel expands them, and the attention kernel
 (plus the merge kernel when keys are split) verifies every node of every tree.  The host
-builder of step k+1 overlaps the device work of step k (double-buffered pinned arrays).
+builder of step k+1 overlaps the device work of step k (double-buffered pinned arrays),
+and so do its parent copy and metadata kernel (on a side stream).
 
 Default workload: B=64 requests, prefix L=4096, N=33-node random draft trees (depth <= 8),
 GQA 32 query / 8 kv heads, D=128, bf16, contiguous KV -- 1.117 GB of algorithmic traffic
@@ -324,8 +325,15 @@ def main():
     ws_bytes = tv.tree_verify_attn_workspace_size(q, k, v, parent_dev[0], prefix_dev, Lmax,
                                                   page_table=pt_dev, page_size=page)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    # The parent copy and the metadata kernel of a step run on a side stream (default
+    # priority), overlapping the previous step's attention; the attention of a step waits
+    # only for its own parent array.  Two parent slots: slot s is refilled only after the
+    # attention that last read it has finished.
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
     copy_done = [torch.cuda.Event() for _ in range(2)]
-    for e in copy_done:
+    att_done = [torch.cuda.Event() for _ in range(2)]
+    for e in copy_done + att_done:
         e.record()
     total = args.warmup + args.steps
     ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(total)]
@@ -336,16 +344,20 @@ def main():
         copy_done[s].synchronize()        # the copy that last read this pinned slot is done
         tv.tree_meta_build_batch(packed, L, N, parent=pin_np[s], depth=h_depth,
                                  bitmask=h_mask, pos=h_pos)
-        parent_dev[s].copy_(pin[s], non_blocking=True)
-        copy_done[s].record()
-        tv.tree_meta_from_parent(parent_dev[s], prefix_dev, depth=d_depth, bitmask=d_mask,
-                                 pos=d_pos)
+        with torch.cuda.stream(side):
+            side.wait_event(att_done[s])
+            parent_dev[s].copy_(pin[s], non_blocking=True)
+            copy_done[s].record()
+            tv.tree_meta_from_parent(parent_dev[s], prefix_dev, depth=d_depth, bitmask=d_mask,
+                                     pos=d_pos)
+        main.wait_event(copy_done[s])
         qi, ki, vi = qkv[i % n_copies]
         ev_a[i].record()
         tv.tree_verify_attn(qi, ki, vi, parent_dev[s], prefix_dev, Lmax, page_table=pt_dev,
                             page_size=page, out=out, lse=lse, workspace=ws,
                             rope_theta=args.rope_theta)
         ev_b[i].record()
+        att_done[s].record()
 
     print("[bench] warmup", file=sys.stderr, flush=True)
     for i in range(args.warmup):
