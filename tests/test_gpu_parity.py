@@ -303,6 +303,19 @@ def test_long_context_paged_sampled(B):
     c.check(out, lse, requests=_sampled(B)[:3])
 
 
+@pytest.mark.parametrize("page_size", [1, 8, 12, 32, 64, 256])
+@pytest.mark.parametrize("D", [64, 128])
+def test_paged_page_sizes(page_size, D):
+    # power-of-two pages holding whole 1 KB load instructions take the wave-uniform page
+    # lookup; 1- and 12-token pages the per-lane path; prefixes not page-aligned
+    paths, _ = random_trees(2000 + page_size, 3, 33, 8)
+    c = Case(f"paged_ps{page_size}_d{D}", [900, 33, 517], trees=paths, D=D,
+             seed=2100 + page_size + D, page_size=page_size, page_seed=3100 + page_size)
+    for splits in (0, 2):
+        out, lse = c.run(num_splits=splits)
+        c.check(out, lse)
+
+
 def test_paged_small_full_with_splits():
     spec = workloads.WORKLOADS["long_paged_n33"]
     trees, _ = workloads.trees_for(spec, batch=4)

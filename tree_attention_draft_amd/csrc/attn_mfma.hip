@@ -164,6 +164,11 @@ struct LoadPlan {
     r = ik * C::RPI + lane / C::CH;
     coff = ((lane % C::CH) ^ (v ? swz_v<C::CH>(r) : swz_k<C::CH>(r))) * 16;
   }
+  // first tile row that instruction ii of wave w copies (wave-uniform)
+  __device__ inline int first_row(int ii, int w) const {
+    const int ik = kSplit ? (ii % HALF) * NW + w : (is_v(ii) ? w - C::LI / 2 : w);
+    return ik * C::RPI;
+  }
   // LDS byte offset of instruction ii within a stage
   __device__ inline uint32_t dst(int ii) const {
     if constexpr (kSplit) return dst0 + (ii >= HALF ? C::TILEB : 0) + (ii % HALF) * NW * 1024;
@@ -184,14 +189,18 @@ struct LoadPlan {
 
 // Issue the direct loads of the tile at logical key kt0 into the stage at LDS address
 // `stage`.  Full tiles of contiguous KV (`fast`: the per-lane offsets fit 32 bits) use a
-// scalar tile base plus the precomputed lane offsets.  Otherwise (paged KV, or the last,
-// partial tile) rows at or past kend are redirected to key kend-1 (finite data, masked
-// out later), so every LDS slot of the stage is rewritten and no read leaves [0, kend).
+// scalar tile base plus the precomputed lane offsets.  Full tiles of paged KV whose pages
+// hold a whole number of one instruction's rows (`pfast`: page size a power of two and a
+// multiple of RPI) do the same with one page lookup per instruction: the RPI rows an
+// instruction copies lie in one page, so its base is wave-uniform.  Otherwise (the last,
+// partial tile, or other page sizes) rows at or past kend are redirected to key kend-1
+// (finite data, masked out later), so every LDS slot of the stage is rewritten and no read
+// leaves [0, kend).
 template <class C, int NW, int KT>
 __device__ inline void issue_tile(const AttnParams& p, const RowMap& rm,
                                   const LoadPlan<C, NW>& lp, const char* kg, const char* vg,
-                                  uint32_t stage, int kt0, int kend, bool fast, int w,
-                                  int lane) {
+                                  uint32_t stage, int kt0, int kend, bool fast, bool pfast,
+                                  int w, int lane) {
   if (fast && kt0 + KT <= kend) {
     const int64_t row0 = (rm.head_off + (int64_t)kt0 * p.kv_st) * 2;
     const char* kb = kg + row0;
@@ -199,6 +208,23 @@ __device__ inline void issue_tile(const AttnParams& p, const RowMap& rm,
 #pragma unroll
     for (int ii = 0; ii < C::LPW; ++ii)
       lds_load16_s(lp.is_v(ii) ? vb : kb, lp.off[ii], stage + lp.dst(ii));
+    return;
+  }
+  if (pfast && kt0 + KT <= kend) {
+    // one LDS read for all of the wave's instructions: lane i fetches instruction i's page
+    const int li = lane < C::LPW ? lane : 0;
+    const int lpage = rm.pt[((kt0 + lp.first_row(li, w)) >> p.page_shift) - rm.pbase];
+#pragma unroll
+    for (int ii = 0; ii < C::LPW; ++ii) {
+      const int r0 = lp.first_row(ii, w);
+      const int t0 = kt0 + r0;
+      const int page = __builtin_amdgcn_readlane(lpage, ii);
+      // element offset of tile row 0 as if the page continued backwards: lp.off holds the
+      // lane's row r0 + lane/CH relative to row 0
+      const int64_t el = (int64_t)page * p.kv_sb + rm.head_off +
+                         (int64_t)((t0 & (p.page_size - 1)) - r0) * p.kv_st;
+      lds_load16_s((lp.is_v(ii) ? vg : kg) + el * 2, lp.off[ii], stage + lp.dst(ii));
+    }
     return;
   }
 #pragma unroll
@@ -506,12 +532,14 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
 
   // ---- start the first two windows streaming ----
   const LoadPlan<C, NW> lp(p, w, lane);
-  const bool fast = !p.paged && (int64_t)(KT - 1) * p.kv_st * 2 + 2 * D <= INT32_MAX;
+  const bool off32 = (int64_t)(KT - 1) * p.kv_st * 2 + 2 * D <= INT32_MAX;
+  const bool fast = !p.paged && off32;
+  const bool pfast = p.paged && off32 && p.page_shift >= 0 && p.page_size % C::RPI == 0;
 #pragma unroll
   for (int s = 0; s < NST; ++s)
     if (s < ntiles)
       issue_tile<C, NW, KT>(p, rm, lp, kg, vg, sbase + s * C::STAGEB, kbeg + s * KT, kend, fast,
-                            w, lane);
+                            pfast, w, lane);
 
   f32x4 o[TT][DB];
   f32x4 nm4[TT];
@@ -650,7 +678,7 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
         const int tn = it + WIN + s;
         if (tn < ntiles)
           issue_tile<C, NW, KT>(p, rm, lp, kg, vg, sbase + (tn % NST) * C::STAGEB,
-                                kbeg + tn * KT, kend, fast, w, lane);
+                                kbeg + tn * KT, kend, fast, pfast, w, lane);
       }
     }
     if (ROPE && kbeg + (it + WIN) * KT > L) {  // the window holds tree keys (uniform)
