@@ -323,7 +323,8 @@ def main():
     out = torch.empty_like(q)
     lse = torch.empty((B, N, Hq), dtype=torch.float32, device=dev)
     ws_bytes = tv.tree_verify_attn_workspace_size(q, k, v, parent_dev[0], prefix_dev, Lmax,
-                                                  page_table=pt_dev, page_size=page)
+                                                  page_table=pt_dev, page_size=page,
+                                                  prefix_len_host=L)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     # The parent copy and the metadata kernel of a step run on a side stream (default
     # priority), overlapping the previous step's attention; the attention of a step waits
@@ -355,7 +356,7 @@ def main():
         ev_a[i].record()
         tv.tree_verify_attn(qi, ki, vi, parent_dev[s], prefix_dev, Lmax, page_table=pt_dev,
                             page_size=page, out=out, lse=lse, workspace=ws,
-                            rope_theta=args.rope_theta)
+                            rope_theta=args.rope_theta, prefix_len_host=L)
         ev_b[i].record()
         att_done[s].record()
 

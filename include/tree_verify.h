@@ -35,7 +35,7 @@ extern "C" {
 #endif
 
 #define TV_MAX_NODES 64
-#define TV_ABI_VERSION 2
+#define TV_ABI_VERSION 3
 
 typedef enum {
   TV_OK = 0,
@@ -148,6 +148,14 @@ tv_status tree_meta_from_parent(const int32_t* parent, int32_t parent_sb, int32_
  *        form: features (m, m + D/2), m < D/2, turn by angle pos * rope_theta^(-2m/D)
  *        (angle reduced in fp64, cos/sin in fp32).  Nothing is written back: the tree rows
  *        stay unrotated in the cache until tree_kv_compact rotates the accepted ones.
+ *   prefix_len_host: NULL, or a host array holding the same B prefix lengths as the device
+ *        prefix_len (values are clamped to 0..max_prefix_len).  Read on the host only, by
+ *        tree_verify_attn and tree_verify_attn_workspace_size, to plan the automatic split:
+ *        the key chunk is sized to the batch's total work rather than to max_prefix_len,
+ *        and when lengths differ (B <= 256, bf16 matrix-core path) the workgroups take the
+ *        requests longest first.  Results never depend on it: every split count covers
+ *        max_prefix_len + N keys, and a hint that disagrees with the device values only
+ *        costs balance.  The caller owns it; it is not retained after the call.
  */
 typedef struct tv_attn_args {
   int32_t dtype;           /* tv_dtype of q, k, v and out                                  */
@@ -174,14 +182,15 @@ typedef struct tv_attn_args {
   int32_t num_splits;
   int32_t path;            /* tv_path                                                       */
   double rope_theta;       /* 0: none; > 0: fused rotary embedding at L + depth (above)     */
+  const int32_t* prefix_len_host; /* optional HOST copy of prefix_len[B], or NULL (below)    */
 } tv_attn_args;
 
 /*
  * tree_verify_attn_workspace_size -- bytes of device workspace the call needs for these
  * arguments (0 when one split covers every request).  Host only; depends on shapes,
- * strides, max_prefix_len, num_splits and path only (pointer fields are not read), and the
- * automatic split count on the current device's compute-unit count.  Returns 0 for
- * shapes tree_verify_attn would reject.
+ * strides, max_prefix_len, num_splits, path and prefix_len_host only (no other pointer
+ * field is read), and the automatic split count on the current device's compute-unit
+ * count.  Returns 0 for shapes tree_verify_attn would reject.
  */
 size_t tree_verify_attn_workspace_size(const tv_attn_args* a);
 

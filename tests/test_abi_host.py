@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_struct_and_version():
     L = tv.lib()
-    assert L.tv_abi_version() == 2
+    assert L.tv_abi_version() == 3
     assert L.tv_attn_args_sizeof() == ctypes.sizeof(TvAttnArgs)
     for code in range(8):
         assert L.tv_status_string(code).decode().startswith("TV_")
@@ -213,6 +213,48 @@ def test_workspace_missing_is_rejected_before_launch():
     assert tv.lib().tree_verify_attn(ctypes.byref(a), None) == 6
     a.workspace, a.workspace_bytes = 1 << 20, need - 4
     assert tv.lib().tree_verify_attn(ctypes.byref(a), None) == 6
+
+
+def ragged_args(lengths, hint):
+    """B=len(lengths) requests, N=33, 32q/8kv, D=128, bf16, bound = max length; the host
+    copy of the lengths is attached only when `hint`."""
+    B = len(lengths)
+    lens = np.asarray(lengths, np.int32)
+    a = base_args(B=B, N=33, max_prefix_len=int(lens.max()), parent_sb=33,
+                  q_sb=33 * 32 * 128, q_sn=32 * 128, o_sb=33 * 32 * 128, o_sn=32 * 128)
+    if hint:
+        a._hint = lens
+        a.prefix_len_host = lens.ctypes.data
+    return a
+
+
+def test_split_plan_from_host_lengths():
+    # (the automatic plan assumes 2 workgroups per compute unit; no GPU here: 256 units)
+    rng = np.random.Generator(np.random.PCG64(7))
+    ragged = rng.integers(512, 8193, size=64)
+    ragged[0] = 8192                        # the bound: 129 key tiles of 64
+    L = tv.lib()
+    R, D, Hkv = 33 * 4, 128, 8
+    # without the lengths the plan sees 64 requests of 8192 keys: they fill the slots
+    assert L.tree_verify_attn_workspace_size(ctypes.byref(ragged_args(ragged, False))) == 0
+    # with them it sizes chunks to two thirds of the average work (44 of 66 key tiles per
+    # workgroup slot) and splits the long requests in up to three
+    work = sum((int(x) + 33 + 63) // 64 for x in ragged) * Hkv
+    avg = -(-work // 512)
+    chunk = (2 * avg + 2) // 3
+    S = -(-129 // chunk)
+    assert S == 3
+    got = L.tree_verify_attn_workspace_size(ctypes.byref(ragged_args(ragged, True)))
+    assert got == 64 * Hkv * S * R * (D + 1) * 4
+    # equal lengths: the hint changes nothing
+    same = np.full(64, 4096)
+    for hint in (False, True):
+        assert L.tree_verify_attn_workspace_size(ctypes.byref(ragged_args(same, hint))) == 0
+    # a small batch splits with or without the lengths
+    small = [2048] * 8
+    a0 = L.tree_verify_attn_workspace_size(ctypes.byref(ragged_args(small, False)))
+    a1 = L.tree_verify_attn_workspace_size(ctypes.byref(ragged_args(small, True)))
+    assert a0 == a1 > 0
 
 
 def test_single_split_needs_no_workspace():

@@ -276,6 +276,25 @@ def test_ragged_small_full():
     c = Case("ragged_small", L, trees=trees[:6], seed=1003)
     out, lse = c.run()
     c.check(out, lse)
+    # with the host copy of the lengths: chunks sized to the total work, requests taken
+    # longest first, short requests written directly, the rest merged
+    out, lse = c.run(prefix_len_host=c.L)
+    c.check(out, lse)
+
+
+@pytest.mark.parametrize("B", [12, 64, 300])
+def test_ragged_host_lengths(B):
+    # lengths from 1 to 3000 (some requests fit one chunk, some need several); B = 300 is
+    # past the longest-first limit of 256 requests
+    rng = np.random.Generator(np.random.PCG64(2300 + B))
+    L = rng.integers(1, 3000, size=B).astype(np.int32)
+    paths, _ = random_trees(2400 + B, B, 17, 6)
+    c = Case(f"ragged_hint_B{B}", L, trees=paths, seed=2500 + B)
+    out, lse = c.run(prefix_len_host=L)
+    c.check(out, lse, requests=None if B <= 12 else _sampled(B) + [int(np.argmax(L))])
+    # a hint that understates the lengths costs balance, never correctness
+    out2, lse2 = c.run(prefix_len_host=np.minimum(L, 100))
+    c.check(out2, lse2, requests=[0, int(np.argmax(L))])
 
 
 def _sampled(B):
@@ -289,8 +308,8 @@ def test_full_size_workloads_sampled(name):
     L = workloads.prefix_lengths(spec)
     c = Case(name, L, trees=trees, Hq=spec["Hq"], Hkv=spec["Hkv"], D=spec["D"],
              seed=1000 + spec["k"], k_scale=spec.get("k_scale", False))
-    out, lse = c.run()
-    c.check(out, lse, requests=_sampled(c.B))
+    out, lse = c.run(prefix_len_host=c.L)   # as the benchmark launches it
+    c.check(out, lse, requests=_sampled(c.B) + [int(np.argmax(c.L))])
 
 
 @pytest.mark.parametrize("B", [1, 16])

@@ -61,6 +61,7 @@ class TvAttnArgs(ctypes.Structure):
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("num_splits", ctypes.c_int32), ("path", ctypes.c_int32),
         ("rope_theta", ctypes.c_double),
+        ("prefix_len_host", ctypes.c_void_p),
     ]
 
 
@@ -272,8 +273,10 @@ def tree_meta_from_parent(parent, prefix_len=None, batch=None, depth=None, bitma
 
 def make_args(q, k, v, parent, prefix_len, max_prefix_len, page_table=None, page_size=0,
               sm_scale=0.0, out=None, lse=None, workspace=None, num_splits=0, path="auto",
-              rope_theta=0.0):
-    """Fill a TvAttnArgs from torch tensors (no allocation, no checks beyond shapes)."""
+              rope_theta=0.0, prefix_len_host=None):
+    """Fill a TvAttnArgs from torch tensors (no allocation, no checks beyond shapes).
+    ``prefix_len_host``: optional host copy of the prefix lengths (int32 numpy array of B
+    values) for the split plan; the returned struct keeps it alive."""
     torch = _torch()
     B, N, Hq, D = q.shape
     Hkv = k.shape[2]
@@ -316,6 +319,12 @@ def make_args(q, k, v, parent, prefix_len, max_prefix_len, page_table=None, page
     a.num_splits = int(num_splits)
     a.path = PATHS[path] if isinstance(path, str) else int(path)
     a.rope_theta = float(rope_theta)
+    if prefix_len_host is not None:
+        hint = np.ascontiguousarray(prefix_len_host, dtype=np.int32)
+        if hint.shape != (B,):
+            raise ValueError("prefix_len_host must hold B values")
+        a._hint = hint
+        a.prefix_len_host = hint.ctypes.data
     return a
 
 
@@ -326,7 +335,8 @@ def tree_verify_attn_workspace_size(q, k, v, parent, prefix_len, max_prefix_len,
 
 def tree_verify_attn(q, k, v, parent, prefix_len, max_prefix_len, *, page_table=None,
                      page_size=0, sm_scale=0.0, out=None, lse=None, workspace=None,
-                     num_splits=0, path="auto", rope_theta=0.0, stream=None):
+                     num_splits=0, path="auto", rope_theta=0.0, prefix_len_host=None,
+                     stream=None):
     """Tree-verification attention.  q [B, N, Hq, D]; k, v [B, S, Hkv, D] (contiguous) or
     [pages, page_size, Hkv, D] with ``page_table`` [B, pages_per_seq]; parent int32 [B, N]
     or [N]; prefix_len int32 [B].  ``rope_theta`` > 0 fuses the rotary embedding: q and
@@ -343,7 +353,7 @@ def tree_verify_attn(q, k, v, parent, prefix_len, max_prefix_len, *, page_table=
     a = make_args(q, k, v, parent, prefix_len, max_prefix_len, page_table=page_table,
                   page_size=page_size, sm_scale=sm_scale, out=out, lse=lse,
                   workspace=workspace, num_splits=num_splits, path=path,
-                  rope_theta=rope_theta)
+                  rope_theta=rope_theta, prefix_len_host=prefix_len_host)
     need = int(lib().tree_verify_attn_workspace_size(ctypes.byref(a)))
     if need > 0 and (workspace is None or a.workspace_bytes < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)

@@ -314,12 +314,12 @@ __device__ inline float exp_pack(const f32x4 (&sacc)[KB], float c, bf16x8 (&pk)[
 
 // Final store of one row: normalised output and natural-log LSE, or the split partial.
 template <int D>
-__device__ inline void store_row_block(const AttnParams& p, int b, int hkv, int split,
-                                       int node, int head, int row, int lh,
+__device__ inline void store_row_block(const AttnParams& p, bool direct, int b, int hkv,
+                                       int split, int node, int head, int row, int lh,
                                        const f32x4 (&o)[D / 16], float m, float lt) {
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const float lse2 = lt > 0.f ? m + log2f(lt) : -INFINITY;
-  if (p.num_splits == 1) {
+  if (direct) {
     uint16_t* out = static_cast<uint16_t*>(p.out) + (int64_t)b * p.o_sb +
                     (int64_t)node * p.o_sn + (int64_t)head * p.o_sh;
 #pragma unroll
@@ -440,9 +440,11 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
   const int hkv = blockIdx.y % p.Hkv;
   const int hc = (blockIdx.y / p.Hkv) % p.head_chunks;
   const int t0 = (blockIdx.y / p.Hkv / p.head_chunks) * TN;  // first 16-node tile of this wg
-  const int b = blockIdx.z;
+  static_assert(2 * kMaxLptBatch <= kMaxPageSlice, "request order fits the page slice");
+  const int b = p.lpt ? lpt_request(p, blockIdx.z, pt_s, tid, NW * 64) : blockIdx.z;
   const int L = clamped_prefix(p, b);
   const int Ttot = L + p.N;
+  const bool direct = single_split(p, Ttot);  // no merge for this request
   const int kbeg = split * p.chunk;
   if (kbeg >= Ttot) return;  // this request has fewer splits than the grid
   const int kend = min(kbeg + p.chunk, Ttot);
@@ -703,7 +705,8 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
       lt += __shfl_xor(lt, 32);
       const int node = (t0 + t) * 16 + lr;
       if (node < p.N)
-        store_row_block<D>(p, b, hkv, split, node, head, node * p.g + j, lh, o[t], m[t], lt);
+        store_row_block<D>(p, direct, b, hkv, split, node, head, node * p.g + j, lh, o[t],
+                           m[t], lt);
     }
   }
   if constexpr (RR) {
@@ -745,7 +748,7 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
       const int hd = hkv * p.g + row % p.g;
       const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
       const float lse2 = Ls > 0.f ? M + log2f(Ls) : -INFINITY;
-      if (p.num_splits == 1) {
+      if (direct) {
         uint16_t* out = static_cast<uint16_t*>(p.out) + (int64_t)b * p.o_sb +
                         (int64_t)node * p.o_sn + (int64_t)hd * p.o_sh + 4 * q4;
         bf16x4 v;

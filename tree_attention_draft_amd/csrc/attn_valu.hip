@@ -160,7 +160,7 @@ __global__ void __launch_bounds__(256) tv_attn_valu_kernel(AttnParams p) {
     __syncthreads();
   }
 
-  const bool single = p.num_splits == 1;
+  const bool single = single_split(p, Ttot);
 #pragma unroll
   for (int j = 0; j < RPW; ++j) {
     const float lsum = wave_sum(l[j]);

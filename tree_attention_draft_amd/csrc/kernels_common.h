@@ -69,6 +69,37 @@ __device__ inline int clamped_prefix(const AttnParams& p, int b) {
   return min(max(p.prefix_len[b], 0), p.max_prefix_len);
 }
 
+// Whether request b (Ttot = L_b + N keys) is covered by a single split: its workgroup
+// then writes the final output itself and the merge leaves the request alone.
+__device__ inline bool single_split(const AttnParams& p, int Ttot) {
+  return p.num_splits == 1 || Ttot <= p.chunk;
+}
+
+// Request served by workgroup slot z when requests are taken longest first (ties: lower
+// index first), so that the longest requests' workgroups are dispatched first and a ragged
+// batch finishes together.  Every thread of the workgroup calls it; it ranks the B <=
+// kMaxLptBatch clamped prefix lengths in `scratch` (2 * kMaxLptBatch ints of LDS).
+__device__ inline int lpt_request(const AttnParams& p, int z, int32_t* scratch, int tid,
+                                  int nthreads) {
+  int32_t* len = scratch;
+  int32_t* order = scratch + kMaxLptBatch;
+  for (int i = tid; i < p.B; i += nthreads) len[i] = clamped_prefix(p, i);
+  __syncthreads();
+  for (int j = tid; j < p.B; j += nthreads) {
+    const int lj = len[j];
+    int rank = 0;
+    for (int i = 0; i < p.B; ++i) {
+      const int li = len[i];
+      rank += (li > lj) || (li == lj && i < j);
+    }
+    order[rank] = j;
+  }
+  __syncthreads();
+  const int b = order[z];
+  __syncthreads();  // the scratch is reused
+  return b;
+}
+
 // Allowed-key bits of one 64-key tile that starts at logical key kt0, for a row whose
 // node has ancestor-or-self bitmask `anc` (bit i <-> tree key L + i).  Bit j is set iff key
 // kt0 + j is a prefix key (< L) or the tree key of an ancestor-or-self.  Keys at or past

@@ -5,7 +5,8 @@
 // log-sum-exp (lse_s, -inf when no key of the chunk was allowed).  The combined result is
 //   lse = log2 sum_s 2^lse_s,   out = sum_s 2^(lse_s - lse) * o_s,
 // i.e. the softmax over the union of the chunks.  Requests with fewer splits than the grid
-// contribute only their own ceil((L + N) / chunk) partials.
+// contribute only their own ceil((L + N) / chunk) partials; a request whose keys fit one
+// chunk was written directly by the attention kernel and is skipped here.
 // One thread per (request, kv head, packed row, 4 features).
 #include "kernels_common.h"
 
@@ -25,6 +26,7 @@ __global__ void __launch_bounds__(256) tv_merge_kernel(AttnParams p) {
   const int b = (int)(rest / p.Hkv);
   const int Ttot = clamped_prefix(p, b) + p.N;
   const int ns = min(p.num_splits, (Ttot + p.chunk - 1) / p.chunk);
+  if (ns <= 1) return;  // one split: the attention kernel wrote the final output
 
   const int64_t base = ((int64_t)b * p.Hkv + hkv) * p.num_splits;
   float mx = -INFINITY;

@@ -14,6 +14,7 @@ tv_status fail(tv_status s, const char* detail);
 constexpr int kKeysPerTile = 64;  // split chunks are multiples of this many keys
 constexpr int kMaxPageSlice = 1024;  // page-table entries one MFMA workgroup stages in LDS
 constexpr int kArgSlice = 8192;      // logits of a row per argmax workgroup (one key slot each)
+constexpr int kMaxLptBatch = 256;    // largest batch the longest-first request order covers
 
 // Everything a kernel needs, passed by value.  Strides in elements.
 struct AttnParams {
@@ -45,6 +46,7 @@ struct AttnParams {
   float scale_log2;    // sm_scale * log2(e)
   int32_t rope;        // fused rotary embedding of q and the tree keys at L + depth
   double rope_log2_theta;
+  int32_t lpt;         // MFMA: workgroups take requests longest first (ragged batches)
 };
 
 // MFMA kernel shape: `nw` waves per workgroup, one query head each; every wave owns
