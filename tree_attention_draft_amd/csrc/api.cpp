@@ -162,8 +162,13 @@ tv_status make_plan(const tv_attn_args* a, Plan* pl) {
     // chunks of two thirds of that average, so that its long requests spread over several
     // workgroups taken first (on MI355X, B=64, L ~ U[512, 8192]: 264 us against 281 us
     // with one split and 323 us with chunks of the average)
-    const int64_t slots = 2 * (int64_t)device_cu_count();
-    const int64_t avg = (pair_tiles + slots - 1) / slots;
+    // When that leaves a workgroup under 16 key tiles (small batches), chunks are sized
+    // for one workgroup per compute unit instead: each workgroup pays a prologue and a
+    // partial of R*(D+1)*4 bytes, which short chunks cannot hide (paged L=32768, B=1:
+    // 80 us at 32 splits against 91 us at 57; L=2048, B=8: 26.7 us at 4 against 29.7 at 7).
+    const int64_t cus = device_cu_count();
+    int64_t avg = (pair_tiles + 2 * cus - 1) / (2 * cus);
+    if (avg < 16) avg = (pair_tiles + cus - 1) / cus;
     const int64_t chunk_tiles = std::max<int64_t>(1, ragged ? (2 * avg + 2) / 3 : avg);
     S = (tiles + chunk_tiles - 1) / chunk_tiles;
   }
