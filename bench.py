@@ -2,11 +2,11 @@
 """Benchmark of the tree-verification attention pass on one MI355X.
 
 One step is the whole hot path for one batch: the host C++ builder turns every request's
-candidate rank paths into parent/depth/bitmask/position arrays, the parent arrays are
-copied to the device, the device metadata kernel expands them, and the attention kernel
-(plus the merge kernel when keys are split) verifies every node of every tree.  The host
-builder of step k+1 overlaps the device work of step k (double-buffered pinned arrays),
-and so do its parent copy and metadata kernel (on a side stream).
+candidate rank paths into parent/depth/bitmask/position arrays in pinned host memory, and
+the attention kernel (plus the merge kernel when keys are split) reads the parent arrays
+there in place, expands them into ancestor masks in its prologue (writing depth, bitmask
+and position ids to device arrays as it goes) and verifies every node of every tree.  The
+host builder of step k+1 overlaps the device work of step k (two pinned slots).
 
 Default workload: B=64 requests, prefix L=4096, N=33-node random draft trees (depth <= 8),
 GQA 32 query / 8 kv heads, D=128, bf16, contiguous KV -- 1.117 GB of algorithmic traffic
@@ -316,47 +316,38 @@ def main():
     h_depth = np.empty((B, N), np.int32)
     h_mask = np.empty((B, N), np.uint64)
     h_pos = np.empty((B, N), np.int32)
-    parent_dev = [torch.empty((B, N), dtype=torch.int32, device=dev) for _ in range(2)]
     d_depth = torch.empty((B, N), dtype=torch.int32, device=dev)
     d_mask = torch.empty((B, N), dtype=torch.int64, device=dev)
     d_pos = torch.empty((B, N), dtype=torch.int32, device=dev)
     out = torch.empty_like(q)
     lse = torch.empty((B, N, Hq), dtype=torch.float32, device=dev)
-    ws_bytes = tv.tree_verify_attn_workspace_size(q, k, v, parent_dev[0], prefix_dev, Lmax,
+    ws_bytes = tv.tree_verify_attn_workspace_size(q, k, v, pin[0], prefix_dev, Lmax,
                                                   page_table=pt_dev, page_size=page,
                                                   prefix_len_host=L)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    # The parent copy and the metadata kernel of a step run on a side stream (default
-    # priority), overlapping the previous step's attention; the attention of a step waits
-    # only for its own parent array.  Two parent slots: slot s is refilled only after the
-    # attention that last read it has finished.
-    main = torch.cuda.current_stream()
-    side = torch.cuda.Stream()
-    copy_done = [torch.cuda.Event() for _ in range(2)]
+    # The host builder writes each step's parent arrays into one of two pinned slots and the
+    # pass reads them there in place (no copy, no second stream); the pass also writes the
+    # expanded metadata (depth, bitmask, position ids) from its prologue.  A slot is
+    # rewritten only after the pass that last read it has finished, so the builder of step
+    # k+1 overlaps the pass of step k.
     att_done = [torch.cuda.Event() for _ in range(2)]
-    for e in copy_done + att_done:
+    for e in att_done:
         e.record()
     total = args.warmup + args.steps
     ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(total)]
     ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(total)]
+    meta = (d_depth, d_mask, d_pos)
 
     def step(i):
         s = i % 2
-        copy_done[s].synchronize()        # the copy that last read this pinned slot is done
+        att_done[s].synchronize()         # the pass that last read this pinned slot is done
         tv.tree_meta_build_batch(packed, L, N, parent=pin_np[s], depth=h_depth,
                                  bitmask=h_mask, pos=h_pos)
-        with torch.cuda.stream(side):
-            side.wait_event(att_done[s])
-            parent_dev[s].copy_(pin[s], non_blocking=True)
-            copy_done[s].record()
-            tv.tree_meta_from_parent(parent_dev[s], prefix_dev, depth=d_depth, bitmask=d_mask,
-                                     pos=d_pos)
-        main.wait_event(copy_done[s])
         qi, ki, vi = qkv[i % n_copies]
         ev_a[i].record()
-        tv.tree_verify_attn(qi, ki, vi, parent_dev[s], prefix_dev, Lmax, page_table=pt_dev,
+        tv.tree_verify_attn(qi, ki, vi, pin[s], prefix_dev, Lmax, page_table=pt_dev,
                             page_size=page, out=out, lse=lse, workspace=ws,
-                            rope_theta=args.rope_theta, prefix_len_host=L)
+                            rope_theta=args.rope_theta, prefix_len_host=L, meta=meta)
         ev_b[i].record()
         att_done[s].record()
 
@@ -377,6 +368,11 @@ def main():
     # metadata and a sampled parity check against the oracle (outside the timed region)
     ref_parent = [ometa.build_from_paths(t, 0)["parent"] for t in trees]
     assert all(pin_np[0][b].tolist() == ref_parent[b] for b in range(B))
+    dep_h, msk_h, pos_h = (t.cpu().numpy() for t in meta)
+    for b in range(B):  # the metadata the pass wrote, bit-exact against the oracle
+        ref = ometa.meta_from_parent(ref_parent[b], int(L[b]))
+        assert dep_h[b].tolist() == ref["depth"] and pos_h[b].tolist() == ref["pos"], b
+        assert [int(x) & (2 ** 64 - 1) for x in msk_h[b]] == ref["bitmask"], b
     out_h = out.float().cpu().numpy()
     lse_h = lse.cpu().numpy()
     worst = 0.0

@@ -35,7 +35,7 @@ extern "C" {
 #endif
 
 #define TV_MAX_NODES 64
-#define TV_ABI_VERSION 3
+#define TV_ABI_VERSION 4
 
 typedef enum {
   TV_OK = 0,
@@ -117,8 +117,9 @@ tv_status tree_meta_from_parent(const int32_t* parent, int32_t parent_sb, int32_
                                 uint64_t* bitmask, int32_t* pos, hipStream_t stream);
 
 /*
- * Arguments of tree_verify_attn.  All tensor pointers are device memory; strides are in
- * elements; the last (D) dimension of q, k, v and out is contiguous.
+ * Arguments of tree_verify_attn.  All tensor pointers are device memory (parent may also
+ * be the device address of pinned host memory, see below); strides are in elements; the
+ * last (D) dimension of q, k, v and out is contiguous.
  *
  *   q    [B, N, Hq, D]  at q + b*q_sb + i*q_sn + h*q_sh.
  *   k, v logical token t of request b, kv head g:
@@ -128,7 +129,11 @@ tv_status tree_meta_from_parent(const int32_t* parent, int32_t parent_sb, int32_
  *        Tree node j's key/value is logical token prefix_len[b] + j, in node order
  *        ("Tree attention mask for draft-tree verification", section "What it costs").
  *        Tokens at or beyond prefix_len[b] + N are never read.
- *   parent [B, N] int32 at parent + b*parent_sb (parent_sb = 0: one shared tree).
+ *   parent [B, N] int32 at parent + b*parent_sb (parent_sb = 0: one shared tree).  Read
+ *        once by every workgroup's prologue, so it may live in pinned host memory
+ *        (hipHostMalloc; pass the address hipHostGetDevicePointer gives): a host that
+ *        builds the trees every step then needs no copy.  It must stay unchanged until the
+ *        pass has finished.
  *   prefix_len [B] int32, each in 0..max_prefix_len; max_prefix_len is a host-side upper
  *        bound used only to size the grid (no device sync).
  *   out  [B, N, Hq, D] (same dtype as q) at out + b*o_sb + i*o_sn + h*o_sh.
@@ -156,6 +161,11 @@ tv_status tree_meta_from_parent(const int32_t* parent, int32_t parent_sb, int32_
  *        requests longest first.  Results never depend on it: every split count covers
  *        max_prefix_len + N keys, and a hint that disagrees with the device values only
  *        costs balance.  The caller owns it; it is not retained after the call.
+ *   meta_depth, meta_bitmask, meta_pos: NULL, or device arrays [B, N] (dense) that
+ *        receive what tree_meta_from_parent writes for the same parent and prefix_len
+ *        (depth, ancestor bitmask, prefix_len[b] + depth; -1 / 0 / -1 for invalid nodes).
+ *        The pass expands the parent arrays in its prologue anyway; one workgroup per
+ *        request writes them out, so a caller that wants both needs no second launch.
  */
 typedef struct tv_attn_args {
   int32_t dtype;           /* tv_dtype of q, k, v and out                                  */
@@ -183,6 +193,9 @@ typedef struct tv_attn_args {
   int32_t path;            /* tv_path                                                       */
   double rope_theta;       /* 0: none; > 0: fused rotary embedding at L + depth (above)     */
   const int32_t* prefix_len_host; /* optional HOST copy of prefix_len[B], or NULL (below)    */
+  int32_t* meta_depth;     /* optional [B, N] outputs of the expanded tree (above), or NULL  */
+  uint64_t* meta_bitmask;
+  int32_t* meta_pos;
 } tv_attn_args;
 
 /*
@@ -400,6 +413,15 @@ const char* tv_status_string(tv_status s);
 
 /* Detail of the last error raised on the calling thread ("" if none). */
 const char* tv_last_error(void);
+
+/*
+ * tv_pinned_device_address -- the device address of pinned host memory (hipHostMalloc), as
+ * hipHostGetDevicePointer gives it: what tree_verify_attn's parent field takes when the
+ * host writes the parent arrays every step and the pass reads them in place.  Host only.
+ * Errors: TV_ERR_INVALID_ARG (NULL argument), TV_ERR_HIP (not pinned host memory; *device
+ * is then NULL).
+ */
+tv_status tv_pinned_device_address(const void* host, const void** device);
 
 /* TV_ABI_VERSION of the loaded library. */
 int32_t tv_abi_version(void);

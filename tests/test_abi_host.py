@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_struct_and_version():
     L = tv.lib()
-    assert L.tv_abi_version() == 3
+    assert L.tv_abi_version() == 4
     assert L.tv_attn_args_sizeof() == ctypes.sizeof(TvAttnArgs)
     for code in range(8):
         assert L.tv_status_string(code).decode().startswith("TV_")

@@ -75,6 +75,86 @@ def test_meta_from_parent_shared_tree_and_invalid_nodes():
     assert int(bitmask[0, 1]) == 0b11 and int(bitmask[0, 2]) == 0
 
 
+def _meta_ref(parents, L):
+    return [ometa.meta_from_parent(list(par), int(Lb)) for par, Lb in zip(parents, L)]
+
+
+def _meta_outputs(B, N):
+    return (torch.full((B, N), -7, dtype=torch.int32, device="cuda"),
+            torch.full((B, N), -7, dtype=torch.int64, device="cuda"),
+            torch.full((B, N), -7, dtype=torch.int32, device="cuda"))
+
+
+def _assert_meta(meta, refs):
+    depth, bitmask, pos = (t.cpu().numpy() for t in meta)
+    for b, ref in enumerate(refs):
+        assert depth[b].tolist() == ref["depth"], b
+        assert pos[b].tolist() == ref["pos"], b
+        assert [int(x) & (2 ** 64 - 1) for x in bitmask[b]] == ref["bitmask"], b
+
+
+@pytest.mark.parametrize("shape", ["mfma_splits", "mfma_longest_first", "mfma_node_chunks",
+                                   "valu_f32"])
+def test_pass_exports_tree_metadata(shape):
+    # the pass expands the parent arrays in its prologue; written out, that expansion
+    # equals the oracle's metadata bit for bit and leaves out/lse bit-identical
+    if shape == "mfma_splits":
+        paths, _ = random_trees(2600, 5, 33, 8)
+        c = Case("meta_export_splits", [100, 900, 0, 513, 64], trees=paths, seed=2601)
+        kw = dict(num_splits=3)
+    elif shape == "mfma_longest_first":
+        rng = np.random.Generator(np.random.PCG64(2602))
+        L = rng.integers(1, 2000, size=12).astype(np.int32)
+        paths, _ = random_trees(2603, 12, 17, 6)
+        c = Case("meta_export_lpt", L, trees=paths, seed=2604)
+        kw = dict(prefix_len_host=L)
+    elif shape == "mfma_node_chunks":
+        paths, _ = random_trees(2605, 3, 64, 10)
+        c = Case("meta_export_n64", [300, 40, 1000], trees=paths, Hq=64, Hkv=8, seed=2606)
+        kw = {}
+    else:
+        c = Case("meta_export_f32", [16, 3, 40], trees=TEN, Hq=1, Hkv=1, D=64, dtype="f32",
+                 seed=2607)
+        kw = dict(num_splits=2)
+    out0, lse0 = c.run(**kw)
+    meta = _meta_outputs(c.B, c.N)
+    out1, lse1 = c.run(meta=meta, **kw)
+    _assert_meta(meta, _meta_ref(c.parent_oracle, c.L))
+    assert np.array_equal(out0, out1) and np.array_equal(lse0, lse1)
+    c.check(out1, lse1)
+
+
+def test_pass_exports_flag_invalid_nodes():
+    # broken parent conventions: the export flags them node by node exactly as the
+    # standalone kernel does (the attention results of such trees are unspecified)
+    bad = [[-1, 0, 2, 1, 7], [-1, 0, 1, -1, 3], [-1, 0, 0, 1, 2]]
+    c = Case("meta_export_invalid", [20, 50, 8], parents=bad, Hq=4, Hkv=1, D=64, seed=2608)
+    meta = _meta_outputs(c.B, c.N)
+    c.run(meta=meta)
+    P = torch.tensor(np.array(bad, np.int32)).cuda()
+    ref = tv.tree_meta_from_parent(P, c.device()["prefix_len"])
+    for got, want in zip(meta, ref):
+        assert torch.equal(got, want)
+    assert meta[0].cpu().tolist()[0] == [0, 1, -1, 2, -1]
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D", [("bf16", 32, 8, 128), ("f32", 2, 1, 64)])
+def test_pinned_host_parent_read_in_place(dtype, Hq, Hkv, D):
+    # the parent arrays may stay in pinned host memory: the pass reads them in place
+    paths, _ = random_trees(2610, 4, 33, 8)
+    c = Case(f"pinned_parent_{dtype}", [300, 1000, 77, 2048], trees=paths, Hq=Hq, Hkv=Hkv,
+             D=D, dtype=dtype, seed=2611)
+    out_d, lse_d = c.run(num_splits=2)
+    host_parent = torch.tensor(np.array(c.parent_gpu, np.int32)).pin_memory()
+    meta = _meta_outputs(c.B, c.N)
+    out_h, lse_h = c.run(parent=host_parent, num_splits=2, meta=meta)
+    assert np.array_equal(out_d, out_h) and np.array_equal(lse_d, lse_h)
+    _assert_meta(meta, _meta_ref(c.parent_oracle, c.L))
+    c.check(out_h, lse_h)
+    with pytest.raises(ValueError):
+        c.run(parent=torch.tensor(np.array(c.parent_gpu, np.int32)))  # pageable host memory
+
+
 # ------------------------------------------------------------------ worked example ----
 @pytest.mark.parametrize("tree", ["tree10", "empty", "chain5"])
 @pytest.mark.parametrize("splits", [0, 1, 2])

@@ -28,7 +28,7 @@ EXPORTS = ["tree_meta_build", "tree_meta_build_batch", "tree_meta_from_parent",
            "tree_accept_greedy_workspace_size",
            "tree_kv_compact", "tree_expected_tokens", "tree_ridge_tokens",
            "tree_budget_nodes", "tree_best_static", "tree_budget_plan",
-           "tv_status_string", "tv_last_error", "tv_abi_version",
+           "tv_status_string", "tv_last_error", "tv_abi_version", "tv_pinned_device_address",
            "tv_attn_args_sizeof", "tv_accept_args_sizeof", "tv_compact_args_sizeof"]
 
 
@@ -62,6 +62,8 @@ class TvAttnArgs(ctypes.Structure):
         ("num_splits", ctypes.c_int32), ("path", ctypes.c_int32),
         ("rope_theta", ctypes.c_double),
         ("prefix_len_host", ctypes.c_void_p),
+        ("meta_depth", ctypes.c_void_p), ("meta_bitmask", ctypes.c_void_p),
+        ("meta_pos", ctypes.c_void_p),
     ]
 
 
@@ -125,6 +127,8 @@ def lib():
     L.tv_last_error.restype = ctypes.c_char_p
     L.tv_last_error.argtypes = []
     L.tv_abi_version.restype = i32
+    L.tv_pinned_device_address.restype = i32
+    L.tv_pinned_device_address.argtypes = [vp, ctypes.POINTER(vp)]
     L.tv_attn_args_sizeof.restype = ctypes.c_size_t
     L.tree_accept_greedy_workspace_size.restype = ctypes.c_size_t
     L.tree_accept_greedy_workspace_size.argtypes = [ctypes.POINTER(TvAcceptArgs)]
@@ -241,6 +245,19 @@ def _require_cuda(*tensors):
             raise ValueError("tree-verify device entry points take GPU tensors")
 
 
+def _parent_address(parent):
+    """Address the kernels read ``parent`` at: a GPU tensor's own, or the device address of
+    a pinned host tensor (the pass reads it in place, so the host may refill such a buffer
+    only after the pass that reads it has finished)."""
+    if parent.is_cuda:
+        return parent.data_ptr()
+    if not parent.is_pinned():
+        raise ValueError("parent must be a GPU tensor or a pinned host tensor")
+    dev = ctypes.c_void_p()
+    _check(lib().tv_pinned_device_address(ctypes.c_void_p(parent.data_ptr()), ctypes.byref(dev)))
+    return dev.value
+
+
 def tree_meta_from_parent(parent, prefix_len=None, batch=None, depth=None, bitmask=None,
                           pos=None, stream=None):
     """Device metadata from int32 parent arrays ``[B, N]`` (or ``[N]`` shared by ``batch``
@@ -273,10 +290,12 @@ def tree_meta_from_parent(parent, prefix_len=None, batch=None, depth=None, bitma
 
 def make_args(q, k, v, parent, prefix_len, max_prefix_len, page_table=None, page_size=0,
               sm_scale=0.0, out=None, lse=None, workspace=None, num_splits=0, path="auto",
-              rope_theta=0.0, prefix_len_host=None):
+              rope_theta=0.0, prefix_len_host=None, meta=None):
     """Fill a TvAttnArgs from torch tensors (no allocation, no checks beyond shapes).
     ``prefix_len_host``: optional host copy of the prefix lengths (int32 numpy array of B
-    values) for the split plan; the returned struct keeps it alive."""
+    values) for the split plan; the returned struct keeps it alive.  ``parent`` may be a
+    pinned host tensor (read in place).  ``meta``: optional (depth, bitmask, pos) [B, N]
+    GPU tensors (int32, int64, int32; any may be None) the pass also fills."""
     torch = _torch()
     B, N, Hq, D = q.shape
     Hkv = k.shape[2]
@@ -305,7 +324,7 @@ def make_args(q, k, v, parent, prefix_len, max_prefix_len, page_table=None, page
         a.parent_sb = 0
     else:
         a.parent_sb = parent.stride(0)
-    a.parent = parent.data_ptr()
+    a.parent = _parent_address(parent)
     a.prefix_len = prefix_len.data_ptr()
     a.max_prefix_len = int(max_prefix_len)
     a.sm_scale = float(sm_scale)
@@ -325,6 +344,11 @@ def make_args(q, k, v, parent, prefix_len, max_prefix_len, page_table=None, page
             raise ValueError("prefix_len_host must hold B values")
         a._hint = hint
         a.prefix_len_host = hint.ctypes.data
+    if meta is not None:
+        depth, bitmask, pos = meta
+        a.meta_depth = depth.data_ptr() if depth is not None else None
+        a.meta_bitmask = bitmask.data_ptr() if bitmask is not None else None
+        a.meta_pos = pos.data_ptr() if pos is not None else None
     return a
 
 
@@ -336,15 +360,22 @@ def tree_verify_attn_workspace_size(q, k, v, parent, prefix_len, max_prefix_len,
 def tree_verify_attn(q, k, v, parent, prefix_len, max_prefix_len, *, page_table=None,
                      page_size=0, sm_scale=0.0, out=None, lse=None, workspace=None,
                      num_splits=0, path="auto", rope_theta=0.0, prefix_len_host=None,
-                     stream=None):
+                     meta=None, stream=None):
     """Tree-verification attention.  q [B, N, Hq, D]; k, v [B, S, Hkv, D] (contiguous) or
     [pages, page_size, Hkv, D] with ``page_table`` [B, pages_per_seq]; parent int32 [B, N]
-    or [N]; prefix_len int32 [B].  ``rope_theta`` > 0 fuses the rotary embedding: q and
-    the tree keys are passed unrotated and rotated at L + depth inside the kernels.
-    Returns ``(out, lse)``; ``lse`` is the natural-log log-sum-exp per (request, node,
-    query head)."""
+    or [N] (a GPU tensor, or a pinned host tensor read in place); prefix_len int32 [B].
+    ``rope_theta`` > 0 fuses the rotary embedding: q and the tree keys are passed
+    unrotated and rotated at L + depth inside the kernels.  ``meta``: optional
+    (depth, bitmask, pos) [B, N] GPU tensors that also receive the expanded tree, as
+    ``tree_meta_from_parent`` writes it.  Returns ``(out, lse)``; ``lse`` is the
+    natural-log log-sum-exp per (request, node, query head)."""
     torch = _torch()
-    _require_cuda(q, k, v, parent, prefix_len, page_table, out, lse, workspace)
+    _require_cuda(q, k, v, prefix_len, page_table, out, lse, workspace)
+    if meta is not None:
+        _require_cuda(*meta)
+        for t, dt in zip(meta, (torch.int32, torch.int64, torch.int32)):
+            if t is not None and (t.dtype != dt or t.numel() != B_N(q) or not t.is_contiguous()):
+                raise ValueError("meta outputs must be contiguous [B, N] int32/int64/int32")
     B, N, Hq, D = q.shape
     if out is None:
         out = torch.empty_like(q)
@@ -353,7 +384,7 @@ def tree_verify_attn(q, k, v, parent, prefix_len, max_prefix_len, *, page_table=
     a = make_args(q, k, v, parent, prefix_len, max_prefix_len, page_table=page_table,
                   page_size=page_size, sm_scale=sm_scale, out=out, lse=lse,
                   workspace=workspace, num_splits=num_splits, path=path,
-                  rope_theta=rope_theta, prefix_len_host=prefix_len_host)
+                  rope_theta=rope_theta, prefix_len_host=prefix_len_host, meta=meta)
     need = int(lib().tree_verify_attn_workspace_size(ctypes.byref(a)))
     if need > 0 and (workspace is None or a.workspace_bytes < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -362,6 +393,11 @@ def tree_verify_attn(q, k, v, parent, prefix_len, max_prefix_len, *, page_table=
     st = lib().tree_verify_attn(ctypes.byref(a), _stream(stream))
     _check(st)
     return out, lse
+
+
+def B_N(q):
+    """Elements of a dense [B, N] array for queries ``q`` [B, N, Hq, D]."""
+    return q.shape[0] * q.shape[1]
 
 
 def default_scale(D):

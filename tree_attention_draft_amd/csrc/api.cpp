@@ -239,6 +239,9 @@ AttnParams make_params(const tv_attn_args* a, const Plan& pl) {
   p.rope = a->rope_theta > 0.0;
   p.rope_log2_theta = p.rope ? std::log2(a->rope_theta) : 0.0;
   p.lpt = pl.lpt ? 1 : 0;
+  p.meta_depth = a->meta_depth;
+  p.meta_bitmask = a->meta_bitmask;
+  p.meta_pos = a->meta_pos;
   if (pl.splits > 1) {
     p.ws_o = static_cast<float*>(a->workspace);
     p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + pl.ws_o_bytes);
@@ -463,6 +466,15 @@ extern "C" const char* tv_status_string(tv_status s) {
 }
 
 extern "C" const char* tv_last_error(void) { return g_last_error; }
+
+extern "C" tv_status tv_pinned_device_address(const void* host, const void** device) {
+  if (!host || !device) return fail(TV_ERR_INVALID_ARG, "null argument");
+  void* d = nullptr;
+  const hipError_t e = hipHostGetDevicePointer(&d, const_cast<void*>(host), 0);
+  *device = e == hipSuccess ? d : nullptr;
+  if (e != hipSuccess) return fail(TV_ERR_HIP, hipGetErrorString(e));
+  return TV_OK;
+}
 
 extern "C" int32_t tv_abi_version(void) { return TV_ABI_VERSION; }
 

@@ -492,7 +492,10 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
   if (tid < p.N) {
     bool ok;
     int dd;
-    mask_s[tid] = ancestor_bits(p.parent + (int64_t)b * p.parent_sb, tid, p.N, ok, dd);
+    const uint64_t m = ancestor_bits(p.parent + (int64_t)b * p.parent_sb, tid, p.N, ok, dd);
+    mask_s[tid] = m;
+    // one workgroup per request (split 0, first row chunk of kv head 0) exports the tree
+    if (blockIdx.x == 0 && blockIdx.y == 0) export_node_meta(p, b, tid, m, ok, dd);
   }
 
   RowMap rm;

@@ -60,7 +60,10 @@ __global__ void __launch_bounds__(256) tv_attn_valu_kernel(AttnParams p) {
   if (tid < p.N) {
     bool ok;
     int dd;
-    mask_s[tid] = ancestor_bits(p.parent + (int64_t)b * p.parent_sb, tid, p.N, ok, dd);
+    const uint64_t m = ancestor_bits(p.parent + (int64_t)b * p.parent_sb, tid, p.N, ok, dd);
+    mask_s[tid] = m;
+    // one workgroup per request (split 0, first row chunk of kv head 0) exports the tree
+    if (blockIdx.x == 0 && blockIdx.y == 0) export_node_meta(p, b, tid, m, ok, dd);
   }
   for (int idx = tid; idx < ROWS * D; idx += 256) {
     const int r = idx / D, d = idx - (idx / D) * D;

@@ -46,6 +46,16 @@ __device__ inline uint64_t ancestor_bits(const int32_t* __restrict__ par, int i,
   return m;
 }
 
+// Node i's depth, ancestor bitmask and position id, written to the optional [B, N] outputs
+// of the pass exactly as the standalone metadata kernel writes them.
+__device__ inline void export_node_meta(const AttnParams& p, int b, int i, uint64_t m, bool ok,
+                                        int d) {
+  const int64_t at = (int64_t)b * p.N + i;
+  if (p.meta_depth) p.meta_depth[at] = ok ? d : -1;
+  if (p.meta_bitmask) p.meta_bitmask[at] = ok ? m : 0ull;
+  if (p.meta_pos) p.meta_pos[at] = ok ? p.prefix_len[b] + d : -1;
+}
+
 // Element offset of logical token t of request b, kv head h, in the K or V store.
 __device__ inline int64_t kv_offset(const AttnParams& p, int b, int t, int h) {
   if (p.paged) {
