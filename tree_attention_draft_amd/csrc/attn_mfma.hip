@@ -386,6 +386,18 @@ __device__ inline void rope_tree_keys(char* smem, int it, int ntiles, int kbeg, 
   }
 }
 
+// The same, called out of line: shapes that keep the shared remainder tile hold ~250
+// registers through the loop, and the rotation's fp64 temporaries would otherwise spill
+// loop state.  A spill reload inside the loop waits on the vector-memory counter, which
+// also counts the ring's direct loads, so every reload would drain the ring.
+template <class C, int KT, int NST, int WIN>
+__device__ __noinline__ void rope_tree_keys_outlined(char* smem, int it, int ntiles, int kbeg,
+                                                     int kend, int L, const uint64_t* mask_s,
+                                                     double log2_theta, int tid, int nthreads) {
+  rope_tree_keys<C, KT, NST, WIN>(smem, it, ntiles, kbeg, kend, L, mask_s, log2_theta, tid,
+                                  nthreads);
+}
+
 // Fused rotary embedding of one wave's Q operand registers of tile t (node at position
 // pos): the lane parks its DS operands in a private LDS slot, rotates them there with a
 // plain loop (register arrays take static indices only) and reloads them.  Feature
@@ -687,8 +699,12 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
       }
     }
     if (ROPE && kbeg + (it + WIN) * KT > L) {  // the window holds tree keys (uniform)
-      rope_tree_keys<C, KT, NST, WIN>(smem, it, ntiles, kbeg, kend, L, mask_s,
-                                      p.rope_log2_theta, tid, NW * 64);
+      if constexpr (RR)
+        rope_tree_keys_outlined<C, KT, NST, WIN>(smem, it, ntiles, kbeg, kend, L, mask_s,
+                                                 p.rope_log2_theta, tid, NW * 64);
+      else
+        rope_tree_keys<C, KT, NST, WIN>(smem, it, ntiles, kbeg, kend, L, mask_s,
+                                        p.rope_log2_theta, tid, NW * 64);
       __syncthreads();
     }
     if (!head_on) continue;  // surplus wave of a group smaller than NW: loads only
