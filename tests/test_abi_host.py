@@ -46,6 +46,16 @@ def test_abi_struct_and_version():
         assert L.tv_status_string(code).decode().startswith("TV_")
 
 
+def test_pinned_device_address_rejects_null():
+    # the argument checks come before any runtime call, so they hold without a device
+    L = tv.lib()
+    dev = ctypes.c_void_p(1)
+    assert L.tv_pinned_device_address(None, ctypes.byref(dev)) == 1  # TV_ERR_INVALID_ARG
+    x = ctypes.c_int32(0)
+    assert L.tv_pinned_device_address(ctypes.byref(x), None) == 1
+    assert "null" in L.tv_last_error().decode()
+
+
 # --------------------------------------------------------------- host builder ----
 def rank_paths_from_parent(parent):
     """Rank paths of a parent array: a child's rank is its order among its siblings."""
