@@ -381,6 +381,17 @@ def _sampled(B):
     return sorted(b for b in {0, 1, B // 2, B - 1} if b < B)
 
 
+def _run_as_benchmark(c):
+    """Launch as the benchmark does: parent arrays read in place from pinned host memory,
+    host copy of the lengths for the split plan, metadata written by the pass (checked
+    bit-exactly for every request)."""
+    host_parent = torch.tensor(np.array(c.parent_gpu, np.int32)).pin_memory()
+    meta = _meta_outputs(c.B, c.N)
+    out, lse = c.run(parent=host_parent, prefix_len_host=c.L, meta=meta)
+    _assert_meta(meta, _meta_ref(c.parent_oracle, c.L))
+    return out, lse
+
+
 @pytest.mark.parametrize("name", ["ragged64_n33", "b64_l4096_n33", "wide32_n64"])
 def test_full_size_workloads_sampled(name):
     spec = workloads.WORKLOADS[name]
@@ -388,7 +399,7 @@ def test_full_size_workloads_sampled(name):
     L = workloads.prefix_lengths(spec)
     c = Case(name, L, trees=trees, Hq=spec["Hq"], Hkv=spec["Hkv"], D=spec["D"],
              seed=1000 + spec["k"], k_scale=spec.get("k_scale", False))
-    out, lse = c.run(prefix_len_host=c.L)   # as the benchmark launches it
+    out, lse = _run_as_benchmark(c)
     c.check(out, lse, requests=_sampled(c.B) + [int(np.argmax(c.L))])
 
 
@@ -398,7 +409,7 @@ def test_long_context_paged_sampled(B):
     trees, _ = workloads.trees_for(spec, batch=B)
     L = workloads.prefix_lengths(spec, batch=B)
     c = Case(f"long_paged_B{B}", L, trees=trees, seed=1005, page_size=16, page_seed=3005)
-    out, lse = c.run()
+    out, lse = _run_as_benchmark(c)
     c.check(out, lse, requests=_sampled(B)[:3])
 
 
