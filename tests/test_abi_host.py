@@ -110,6 +110,32 @@ def test_builder_random_workload_trees_and_shuffles():
             assert np.array_equal(ref[k], got[k])
 
 
+@pytest.mark.parametrize("scale,depth", [(1, 8), (127, 8), (128, 8), (1000, 10), (2 ** 30, 3)])
+def test_builder_large_ranks_and_deep_paths(scale, depth):
+    # the builder packs paths into 64-bit keys when ranks x length fit 56 bits (scale 1)
+    # and compares them rank by rank otherwise (the larger scales); both agree with the
+    # oracle, duplicates and shuffled input included
+    rng = np.random.Generator(np.random.PCG64(scale + depth))
+    for n in (5, 33, 64):
+        parent, dep = [-1], [0]
+        for i in range(1, n):
+            choices = [j for j in range(i) if dep[j] < depth]
+            parent.append(int(rng.choice(choices)))
+            dep.append(dep[parent[-1]] + 1)
+        paths = rank_paths_from_parent(parent)
+        paths = [tuple(min(r * scale + (scale - 1 if r else 0), 2 ** 31 - 1) for r in p)
+                 for p in paths]
+        shuffled = list(paths) + [paths[i] for i in rng.integers(0, len(paths), 3)]
+        rng.shuffle(shuffled)
+        assert_same(shuffled, 5)
+    bad = [(0,), (scale, 0), (0, scale)]       # (scale, 0) has no parent (scale,)
+    with pytest.raises(meta.TreeError) as ref:
+        meta.build_from_paths(bad, 0)
+    with pytest.raises(tv.TreeVerifyError) as got:
+        tv.tree_meta_build(bad, 0)
+    assert got.value.bad_path == ref.value.index
+
+
 @pytest.mark.parametrize("paths", [[(0, 0)], [(1,), (0, 1)], [(0,), (2, 0), (0, 0)],
                                    [(0,), (0, 0, 0)], [(3,), (0,), (0, 5, 1), (0, 4)]])
 def test_builder_missing_parent_matches_oracle_index(paths):

@@ -11,7 +11,12 @@
 // Implementation: sort references into the CSR rank arrays (no copies of the paths;
 // thread-local scratch, so a batch allocates nothing per tree), drop adjacent duplicates, and resolve each parent by binary
 // search for the one-shorter prefix among the already-placed nodes of the previous
-// length (they are contiguous and sorted in the node order).
+// length (they are contiguous and sorted in the node order).  When every rank fits b bits
+// and the longest candidate has at most 56/b ranks (drafter trees: a few bits, depth
+// ~10), each candidate is first packed into one 64-bit key -- length in the top byte,
+// ranks below it most significant first at fixed field positions -- so integer order is
+// the (length, lexicographic) order, and a parent's key is the child's with its length
+// decremented and its last field cleared.
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
@@ -56,7 +61,59 @@ struct Scratch {
   std::vector<PathRef> refs, nodes;
   struct Group { int32_t len; int64_t begin, end; };
   std::vector<Group> groups;
+  struct Keyed { uint64_t key; int32_t input_index; };
+  std::vector<Keyed> keyed;
+  std::vector<uint64_t> node_keys;
 };
+
+// The packed-key form of build_one (see the file comment); refs validated, b bits per rank.
+tv_status build_keyed(Scratch& sc, int32_t max_len, int32_t b, int32_t prefix_len,
+                      int32_t cap, int32_t* parent, int32_t* depth, uint64_t* bitmask,
+                      int32_t* pos, int32_t* num_nodes, int32_t* bad) {
+  auto& keyed = sc.keyed;
+  auto& keys = sc.node_keys;
+  keyed.clear();
+  keys.clear();
+  for (const PathRef& r : sc.refs) {
+    uint64_t k = static_cast<uint64_t>(r.len) << 56;
+    for (int32_t t = 0; t < r.len; ++t)
+      k |= static_cast<uint64_t>(r.r[t]) << (b * (max_len - 1 - t));
+    keyed.push_back(Scratch::Keyed{k, r.input_index});
+  }
+  std::sort(keyed.begin(), keyed.end(), [](const Scratch::Keyed& x, const Scratch::Keyed& y) {
+    return x.key != y.key ? x.key < y.key : x.input_index < y.input_index;
+  });
+  keys.push_back(0);  // the root: length 0, no ranks
+  for (size_t i = 0; i < keyed.size(); ++i)
+    if (i == 0 || keyed[i].key != keyed[i - 1].key) keys.push_back(keyed[i].key);
+  const int64_t n = static_cast<int64_t>(keys.size());
+  if (n > cap || n > TV_MAX_NODES)
+    return tv::fail(TV_ERR_CAPACITY, "tree has more nodes than the output capacity");
+  parent[0] = -1;
+  depth[0] = 0;
+  bitmask[0] = 1ull;
+  const uint64_t field = (1ull << b) - 1;
+  size_t first = 0;  // first keyed entry of the current node (its first input occurrence)
+  for (int64_t i = 1; i < n; ++i) {
+    while (keyed[first].key != keys[i]) ++first;
+    const uint64_t k = keys[i];
+    const int32_t len = static_cast<int32_t>(k >> 56);
+    const uint64_t pk = (static_cast<uint64_t>(len - 1) << 56) |
+                        (k & ((1ull << 56) - 1) & ~(field << (b * (max_len - len))));
+    const auto it = std::lower_bound(keys.begin(), keys.begin() + i, pk);
+    if (it == keys.begin() + i || *it != pk) {
+      *bad = keyed[first].input_index;
+      return tv::fail(TV_ERR_MISSING_PARENT, "a path's one-shorter prefix is not a node");
+    }
+    const int64_t found = it - keys.begin();
+    parent[i] = static_cast<int32_t>(found);
+    depth[i] = len;
+    bitmask[i] = bitmask[found] | (1ull << i);
+  }
+  for (int64_t i = 0; i < n; ++i) pos[i] = prefix_len + depth[i];
+  *num_nodes = static_cast<int32_t>(n);
+  return TV_OK;
+}
 
 // One tree from candidates [p0, p1) of a CSR list with absolute offsets path_off[].
 // Writes up to `cap` nodes; *bad gets the offending candidate's index relative to p0.
@@ -69,6 +126,7 @@ tv_status build_one(const int32_t* ranks, const int64_t* path_off, int64_t p0, i
   refs.clear();
   nodes.clear();
   sc.groups.clear();
+  int32_t max_len = 0, max_rank = 0;
   for (int64_t p = p0; p < p1; ++p) {
     const int64_t a = path_off[p], b = path_off[p + 1];
     const int32_t rel = static_cast<int32_t>(p - p0);
@@ -83,9 +141,16 @@ tv_status build_one(const int32_t* ranks, const int64_t* path_off, int64_t p0, i
         *bad = rel;
         return tv::fail(TV_ERR_INVALID_PATH, "negative rank");
       }
+      max_rank = std::max(max_rank, ranks[t]);
     }
+    max_len = std::max(max_len, static_cast<int32_t>(b - a));
     refs.push_back(PathRef{ranks + a, static_cast<int32_t>(b - a), rel});
   }
+  int32_t bits = 1;
+  while (bits < 31 && (max_rank >> bits) != 0) ++bits;
+  if (static_cast<int64_t>(max_len) * bits <= 56)
+    return build_keyed(sc, max_len, bits, prefix_len, cap, parent, depth, bitmask, pos,
+                       num_nodes, bad);
   // (length, lexicographic) order; among duplicates the first input occurrence first
   std::sort(refs.begin(), refs.end(), [](const PathRef& x, const PathRef& y) {
     if (path_less(x, y)) return true;
