@@ -94,7 +94,7 @@ def _assert_meta(meta, refs):
 
 
 @pytest.mark.parametrize("shape", ["mfma_splits", "mfma_longest_first", "mfma_node_chunks",
-                                   "valu_f32"])
+                                   "mfma_rope", "valu_f32"])
 def test_pass_exports_tree_metadata(shape):
     # the pass expands the parent arrays in its prologue; written out, that expansion
     # equals the oracle's metadata bit for bit and leaves out/lse bit-identical
@@ -112,6 +112,10 @@ def test_pass_exports_tree_metadata(shape):
         paths, _ = random_trees(2605, 3, 64, 10)
         c = Case("meta_export_n64", [300, 40, 1000], trees=paths, Hq=64, Hkv=8, seed=2606)
         kw = {}
+    elif shape == "mfma_rope":
+        paths, _ = random_trees(2609, 4, 33, 8)
+        c = Case("meta_export_rope", [700, 31, 64, 1500], trees=paths, seed=2610)
+        kw = dict(rope_theta=10000.0, num_splits=2)
     else:
         c = Case("meta_export_f32", [16, 3, 40], trees=TEN, Hq=1, Hkv=1, D=64, dtype="f32",
                  seed=2607)
