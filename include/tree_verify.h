@@ -158,7 +158,7 @@ tv_status tree_meta_from_parent(const int32_t* parent, int32_t parent_sb, int32_
  *        tree_verify_attn and tree_verify_attn_workspace_size, to plan the automatic split:
  *        the key chunk is sized to the batch's total work rather than to max_prefix_len,
  *        and when lengths differ (B <= 256, bf16 matrix-core path) the workgroups take the
- *        requests longest first.  Results never depend on it: every split count covers
+ *        (request, key chunk) pieces longest first.  Results never depend on it: every split count covers
  *        max_prefix_len + N keys, and a hint that disagrees with the device values only
  *        costs balance.  The caller owns it; it is not retained after the call.
  *   meta_depth, meta_bitmask, meta_pos: NULL, or device arrays [B, N] (dense) that

@@ -448,12 +448,17 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
   const int lr = lane & 15;
   const int lh = lane >> 4;
-  const int split = blockIdx.x;
   const int hkv = blockIdx.y % p.Hkv;
   const int hc = (blockIdx.y / p.Hkv) % p.head_chunks;
   const int t0 = (blockIdx.y / p.Hkv / p.head_chunks) * TN;  // first 16-node tile of this wg
-  static_assert(2 * kMaxLptBatch <= kMaxPageSlice, "request order fits the page slice");
-  const int b = p.lpt ? lpt_request(p, blockIdx.z, pt_s, tid, NW * 64) : blockIdx.z;
+  static_assert(3 * kMaxLptBatch + 1 <= kMaxPageSlice, "piece order fits the page slice");
+  int b = blockIdx.z, split = blockIdx.x;
+  if (p.lpt) {
+    if (!lpt_piece(p, blockIdx.z * gridDim.x + blockIdx.x, pt_s, tid, NW * 64, b, split))
+      return;  // more slots than pieces
+    b = __builtin_amdgcn_readfirstlane(b);
+    split = __builtin_amdgcn_readfirstlane(split);
+  }
   const int L = clamped_prefix(p, b);
   const int Ttot = L + p.N;
   const bool direct = single_split(p, Ttot);  // no merge for this request
@@ -507,7 +512,7 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
     const uint64_t m = ancestor_bits(p.parent + (int64_t)b * p.parent_sb, tid, p.N, ok, dd);
     mask_s[tid] = m;
     // one workgroup per request (split 0, first row chunk of kv head 0) exports the tree
-    if (blockIdx.x == 0 && blockIdx.y == 0) export_node_meta(p, b, tid, m, ok, dd);
+    if (split == 0 && blockIdx.y == 0) export_node_meta(p, b, tid, m, ok, dd);
   }
 
   RowMap rm;

@@ -85,29 +85,63 @@ __device__ inline bool single_split(const AttnParams& p, int Ttot) {
   return p.num_splits == 1 || Ttot <= p.chunk;
 }
 
-// Request served by workgroup slot z when requests are taken longest first (ties: lower
-// index first), so that the longest requests' workgroups are dispatched first and a ragged
-// batch finishes together.  Every thread of the workgroup calls it; it ranks the B <=
-// kMaxLptBatch clamped prefix lengths in `scratch` (2 * kMaxLptBatch ints of LDS).
-__device__ inline int lpt_request(const AttnParams& p, int z, int32_t* scratch, int tid,
-                                  int nthreads) {
-  int32_t* len = scratch;
-  int32_t* order = scratch + kMaxLptBatch;
-  for (int i = tid; i < p.B; i += nthreads) len[i] = clamped_prefix(p, i);
-  __syncthreads();
+// Piece (request b, key chunk `split`) served by workgroup slot `slot` of a ragged batch,
+// longest first over the pieces: every full chunk first (requests in index order), then
+// each request's last chunk, largest first (ties: lower index).  The dispatcher hands the
+// slots out in order, so the long pieces start first and the short last chunks fill the
+// tail.  Returns false for a slot past the last piece.  Every thread of the workgroup calls
+// it; it uses 3 * kMaxLptBatch + 1 ints of LDS `scratch` (B <= kMaxLptBatch).
+__device__ inline bool lpt_piece(const AttnParams& p, int slot, int32_t* scratch, int tid,
+                                 int nthreads, int& b, int& split) {
+  int32_t* last = scratch;                    // keys in request j's last chunk
+  int32_t* order = scratch + kMaxLptBatch;    // requests by last chunk, largest first
+  int32_t* cum = scratch + 2 * kMaxLptBatch;  // full chunks of requests 0 .. j-1 (B + 1)
   for (int j = tid; j < p.B; j += nthreads) {
-    const int lj = len[j];
+    const int T = clamped_prefix(p, j) + p.N;
+    const int n = (T + p.chunk - 1) / p.chunk;  // chunks of request j, >= 1
+    last[j] = T - (n - 1) * p.chunk;
+    cum[j] = n - 1;
+  }
+  __syncthreads();
+  if (tid == 0) {  // exclusive prefix sum in place (B <= 256 LDS words)
+    int c = 0;
+    for (int j = 0; j < p.B; ++j) {
+      const int f = cum[j];
+      cum[j] = c;
+      c += f;
+    }
+    cum[p.B] = c;
+  }
+  for (int j = tid; j < p.B; j += nthreads) {
+    const int lj = last[j];
     int rank = 0;
     for (int i = 0; i < p.B; ++i) {
-      const int li = len[i];
+      const int li = last[i];
       rank += (li > lj) || (li == lj && i < j);
     }
     order[rank] = j;
   }
   __syncthreads();
-  const int b = order[z];
+  const int full = cum[p.B];
+  bool ok = true;
+  if (slot < full) {  // the last request j with cum[j] <= slot owns full chunk slot - cum[j]
+    int lo = 0, hi = p.B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cum[mid] <= slot) lo = mid; else hi = mid - 1;
+    }
+    b = lo;
+    split = slot - cum[lo];
+  } else if (slot - full < p.B) {
+    b = order[slot - full];
+    split = cum[b + 1] - cum[b];  // its last chunk follows its full ones
+  } else {
+    ok = false;
+    b = 0;
+    split = 0;
+  }
   __syncthreads();  // the scratch is reused
-  return b;
+  return ok;
 }
 
 // Allowed-key bits of one 64-key tile that starts at logical key kt0, for a row whose

@@ -46,7 +46,7 @@ struct AttnParams {
   float scale_log2;    // sm_scale * log2(e)
   int32_t rope;        // fused rotary embedding of q and the tree keys at L + depth
   double rope_log2_theta;
-  int32_t lpt;         // MFMA: workgroups take requests longest first (ragged batches)
+  int32_t lpt;         // MFMA: workgroups take (request, chunk) pieces longest first (ragged)
   int32_t* meta_depth;     // optional [B, N] copies of the expanded tree (may be null)
   uint64_t* meta_bitmask;
   int32_t* meta_pos;
