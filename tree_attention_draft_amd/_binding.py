@@ -374,7 +374,8 @@ def tree_verify_attn(q, k, v, parent, prefix_len, max_prefix_len, *, page_table=
     if meta is not None:
         _require_cuda(*meta)
         for t, dt in zip(meta, (torch.int32, torch.int64, torch.int32)):
-            if t is not None and (t.dtype != dt or t.numel() != B_N(q) or not t.is_contiguous()):
+            if t is not None and (t.dtype != dt or t.numel() != _dense_bn(q)
+                                  or not t.is_contiguous()):
                 raise ValueError("meta outputs must be contiguous [B, N] int32/int64/int32")
     B, N, Hq, D = q.shape
     if out is None:
@@ -395,7 +396,7 @@ def tree_verify_attn(q, k, v, parent, prefix_len, max_prefix_len, *, page_table=
     return out, lse
 
 
-def B_N(q):
+def _dense_bn(q):
     """Elements of a dense [B, N] array for queries ``q`` [B, N, Hq, D]."""
     return q.shape[0] * q.shape[1]
 
