@@ -398,21 +398,22 @@ __device__ __noinline__ void rope_tree_keys_outlined(char* smem, int it, int nti
                                   nthreads);
 }
 
-// Fused rotary embedding of one wave's Q operand registers of tile t (node at position
-// pos): the lane parks its DS operands in a private LDS slot, rotates them there with a
-// plain loop (register arrays take static indices only) and reloads them.  Feature
+// Fused rotary embedding of one wave's Q operand registers of one tile: the lane parks its
+// DS operands in a private LDS slot, rotates them there with a plain loop (register arrays
+// take static indices only) by the cos/sin of its node's row `cs_row` (one per feature
+// pair) and reloads them.  Feature
 // m = 32s + 8lh + e sits in operand s, element e; its partner m + D/2 in operand s + DS/2.
 template <int D>
-__device__ inline void rope_q_tile(bf16x8 (&q)[D / 32], char* slot, int pos, int lh,
-                                   double log2_theta) {
+__device__ inline void rope_q_tile(bf16x8 (&q)[D / 32], char* slot, const float2* cs_row,
+                                   int lh) {
   constexpr int DS = D / 32;
 #pragma unroll
   for (int s = 0; s < DS; ++s) *reinterpret_cast<bf16x8*>(slot + 16 * 64 * s) = q[s];
 #pragma unroll 1
   for (int i = 0; i < DS / 2 * 8; ++i) {
     const int s = i / 8, e = i % 8;
-    float cs, sn;
-    rope_cos_sin(pos, 32 * s + 8 * lh + e, D, log2_theta, cs, sn);
+    const float2 t = cs_row[32 * s + 8 * lh + e];
+    const float cs = t.x, sn = t.y;
     __bf16* px = reinterpret_cast<__bf16*>(slot + 16 * 64 * s) + e;
     __bf16* py = reinterpret_cast<__bf16*>(slot + 16 * 64 * (s + DS / 2)) + e;
     float x = static_cast<float>(*px), y = static_cast<float>(*py);
@@ -533,12 +534,33 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
 
   if constexpr (ROPE) {
     // ---- fused rotary embedding of the queries, node i at L + depth(i), in lane-private
-    // LDS slots of the (still idle) ring: DS KB per wave ----
-    static_assert(NW * DS * 1024 <= NST * C::STAGEB, "query slots fit the ring");
+    // LDS slots of the (still idle) ring: DS KB per wave.  The cos/sin of every (node of
+    // this workgroup's tiles, feature pair) are formed once per workgroup into a table
+    // after the slots (the waves' query heads share positions), from the pair frequencies
+    // formed once in fp64. ----
+    constexpr int H = D / 2;
+    static_assert(NW * DS * 1024 + TT * 16 * H * 8 + H * 8 <= NST * C::STAGEB,
+                  "query slots and the cos/sin table fit the ring");
+    const int nbase = t0 * 16;                         // first node of this workgroup's tiles
+    const int nrows = min(p.N - nbase, TT * 16);       // node_of[t] - nbase < nrows
+    float2* cs_tab = reinterpret_cast<float2*>(smem + NW * DS * 1024);
+    double* inv_s = reinterpret_cast<double*>(smem + NW * DS * 1024 + TT * 16 * H * 8);
+    if (tid < H) inv_s[tid] = rope_inv_freq(tid, D, p.rope_log2_theta);
+    __syncthreads();
+    for (int idx = tid; idx < nrows * H; idx += NW * 64) {
+      const int i = idx / H, m = idx - (idx / H) * H;
+      float cs, sn;
+      rope_cos_sin_inv(L + depth_of(mask_s[nbase + i]), inv_s[m], cs, sn);
+      cs_tab[idx] = make_float2(cs, sn);
+    }
+    __syncthreads();
     char* slot = smem + w * DS * 1024 + 16 * lane;
 #pragma unroll
-    for (int t = 0; t < TT; ++t)
-      rope_q_tile<D>(qreg[t], slot, L + depth_of(mask_s[node_of[t]]), lh, p.rope_log2_theta);
+    for (int t = 0; t < TT; ++t) {
+      // only wave 0 parks the shared remainder tile's queries; the others drop theirs
+      if (t >= TN && w != 0) continue;
+      rope_q_tile<D>(qreg[t], slot, cs_tab + (node_of[t] - nbase) * H, lh);
+    }
     __syncthreads();  // the ring may now be overwritten
   }
 

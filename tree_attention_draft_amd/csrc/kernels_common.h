@@ -164,12 +164,20 @@ __device__ inline uint64_t tile_allowed(uint64_t anc, int kt0, int L) {
 // "What interviewers probe next": a tree node is rotated at L + its depth): features m and
 // m + D/2 (m < D/2) turn by angle pos * theta^(-2m/D).  The angle is formed and reduced
 // to [-pi, pi] in fp64 so that long positions keep full fp32 accuracy in cos and sin.
-__device__ inline void rope_cos_sin(int pos, int m, int D, double log2_theta, float& c,
-                                    float& s) {
-  const double inv = exp2(-(2.0 * m / D) * log2_theta);
+__device__ inline double rope_inv_freq(int m, int D, double log2_theta) {
+  return exp2(-(2.0 * m / D) * log2_theta);
+}
+
+// cos and sin of pos * inv, the angle reduced in fp64.
+__device__ inline void rope_cos_sin_inv(int pos, double inv, float& c, float& s) {
   const double a = static_cast<double>(pos) * inv;
   const double r = a - rint(a * 0.15915494309189535) * 6.283185307179586;
   sincosf(static_cast<float>(r), &s, &c);
+}
+
+__device__ inline void rope_cos_sin(int pos, int m, int D, double log2_theta, float& c,
+                                    float& s) {
+  rope_cos_sin_inv(pos, rope_inv_freq(m, D, log2_theta), c, s);
 }
 
 // (x, y) = (x cos - y sin, y cos + x sin): the pair (m, m + D/2) at one angle.
