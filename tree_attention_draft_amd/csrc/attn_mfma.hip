@@ -356,13 +356,14 @@ __device__ inline void wait_tiles(int n) {
 
 // Fused rotary embedding of the tree keys held by the window of tiles it .. it+WIN-1: every
 // K row of logical key t in [L, kend) is rotated in place in LDS at position
-// L + depth(t - L); feature m of row r sits in chunk m/8 of the swizzled row, its partner
+// L + depth(t - L), from the workgroup's pair frequencies `inv_freq`; feature m of row r
+// sits in chunk m/8 of the swizzled row, its partner
 // m + D/2 in chunk m/8 + CH/2.  Called by every thread of the workgroup between the
 // window's publishing barrier and a second barrier; V rows are untouched.  One pair per
 // step and no unrolling, so the few registers it needs fit beside the loop's live state.
 template <class C, int KT, int NST, int WIN>
 __device__ inline void rope_tree_keys(char* smem, int it, int ntiles, int kbeg, int kend,
-                                      int L, const uint64_t* mask_s, double log2_theta,
+                                      int L, const uint64_t* mask_s, const double* inv_freq,
                                       int tid, int nthreads) {
   constexpr int H = C::CH * 4;  // D / 2 pairs per row
   constexpr int D = 2 * H;
@@ -375,7 +376,7 @@ __device__ inline void rope_tree_keys(char* smem, int it, int ntiles, int kbeg, 
     const int tt = (t - kbeg) / KT;
     const int r = (t - kbeg) % KT;
     float cs, sn;
-    rope_cos_sin(L + depth_of(mask_s[t - L]), mm, D, log2_theta, cs, sn);
+    rope_cos_sin_inv(L + depth_of(mask_s[t - L]), inv_freq[mm], cs, sn);
     char* row = smem + (tt % NST) * C::STAGEB + r * C::ROWB + (mm % 8) * 2;
     __bf16* px = reinterpret_cast<__bf16*>(row + (((mm / 8) ^ swz_k<C::CH>(r)) << 4));
     __bf16* py = reinterpret_cast<__bf16*>(row + (((mm / 8 + C::CH / 2) ^ swz_k<C::CH>(r)) << 4));
@@ -393,8 +394,9 @@ __device__ inline void rope_tree_keys(char* smem, int it, int ntiles, int kbeg, 
 template <class C, int KT, int NST, int WIN>
 __device__ __noinline__ void rope_tree_keys_outlined(char* smem, int it, int ntiles, int kbeg,
                                                      int kend, int L, const uint64_t* mask_s,
-                                                     double log2_theta, int tid, int nthreads) {
-  rope_tree_keys<C, KT, NST, WIN>(smem, it, ntiles, kbeg, kend, L, mask_s, log2_theta, tid,
+                                                     const double* inv_freq, int tid,
+                                                     int nthreads) {
+  rope_tree_keys<C, KT, NST, WIN>(smem, it, ntiles, kbeg, kend, L, mask_s, inv_freq, tid,
                                   nthreads);
 }
 
@@ -441,6 +443,8 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
   // the shared remainder tile's query operands (B-operand layout, [k-step][lane]): read
   // from LDS on the key tiles a wave computes it, so they take no registers in the loop
   __shared__ bf16x8 qrem_s[RR ? DS * 64 : 1];
+  // rotary pair frequencies, formed once in fp64 (fused RoPE only)
+  __shared__ double inv_s[ROPE ? D / 2 : 1];
   static_assert(!RR || NW * 16 * D * 4 <= NST * C::STAGEB, "merge buffer fits the ring");
   static_assert(!RR || NW * 16 * 2 <= kMaxPageSlice, "merge (m, l) fits the page slice");
 
@@ -539,12 +543,11 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
     // after the slots (the waves' query heads share positions), from the pair frequencies
     // formed once in fp64. ----
     constexpr int H = D / 2;
-    static_assert(NW * DS * 1024 + TT * 16 * H * 8 + H * 8 <= NST * C::STAGEB,
+    static_assert(NW * DS * 1024 + TT * 16 * H * 8 <= NST * C::STAGEB,
                   "query slots and the cos/sin table fit the ring");
     const int nbase = t0 * 16;                         // first node of this workgroup's tiles
     const int nrows = min(p.N - nbase, TT * 16);       // node_of[t] - nbase < nrows
     float2* cs_tab = reinterpret_cast<float2*>(smem + NW * DS * 1024);
-    double* inv_s = reinterpret_cast<double*>(smem + NW * DS * 1024 + TT * 16 * H * 8);
     if (tid < H) inv_s[tid] = rope_inv_freq(tid, D, p.rope_log2_theta);
     __syncthreads();
     for (int idx = tid; idx < nrows * H; idx += NW * 64) {
@@ -728,10 +731,10 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
     if (ROPE && kbeg + (it + WIN) * KT > L) {  // the window holds tree keys (uniform)
       if constexpr (RR)
         rope_tree_keys_outlined<C, KT, NST, WIN>(smem, it, ntiles, kbeg, kend, L, mask_s,
-                                                 p.rope_log2_theta, tid, NW * 64);
+                                                 inv_s, tid, NW * 64);
       else
-        rope_tree_keys<C, KT, NST, WIN>(smem, it, ntiles, kbeg, kend, L, mask_s,
-                                        p.rope_log2_theta, tid, NW * 64);
+        rope_tree_keys<C, KT, NST, WIN>(smem, it, ntiles, kbeg, kend, L, mask_s, inv_s, tid,
+                                        NW * 64);
       __syncthreads();
     }
     if (!head_on) continue;  // surplus wave of a group smaller than NW: loads only
