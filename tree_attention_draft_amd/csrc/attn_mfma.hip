@@ -34,6 +34,8 @@
 // row-major layout through the transposing LDS read ds_read_b64_tr_b16: within each
 // 16-lane group, lane s addresses V[base + s/4][d0 + 4*(s%4) ..] and output lane l receives
 // V[base + j][d0 + l] for j = 0..3.
+#include <type_traits>
+
 #include "kernels_common.h"
 
 namespace tv {
@@ -80,9 +82,14 @@ __device__ inline void lds_load16_s(const void* base, uint32_t voff, uint32_t ld
 // mostly alternate between matrix and vector work; letting the wave that is issuing MFMAs
 // go first keeps the matrix pipe fed while the other fills the gaps with its vector work.
 // The scheduling barriers keep the compiler from moving instructions across the change.
-__device__ inline void mfma_priority(bool high) {
+// `young`: this workgroup shares its compute unit with an older one that would otherwise
+// win every tie; its vector phases then outrank the older one's (matrix phases still
+// outrank both).
+__device__ inline void mfma_priority(bool high, bool young) {
   __builtin_amdgcn_sched_barrier(0);
   if (high)
+    __builtin_amdgcn_s_setprio(2);
+  else if (young)
     __builtin_amdgcn_s_setprio(1);
   else
     __builtin_amdgcn_s_setprio(0);
@@ -601,13 +608,14 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
   }
 
   // One key tile: S^T = K Q^T, mask, online softmax, O^T += V^T P^T.
-  auto tile = [&](int it, bool do_rem) {
+  auto tile = [&](int it, bool do_rem, auto young_c) {
+    constexpr bool young = decltype(young_c)::value;
     const int kt0 = kbeg + it * KT;
     const char* ks = smem + (it % NST) * C::STAGEB;
     const char* vs = ks + C::TILEB;
 
     // ---- S^T = K Q^T (raised issue priority: see mfma_priority) ----
-    mfma_priority(true);
+    mfma_priority(true, young);
     bf16x8 qr[DS];
     if (RR && do_rem) {
 #pragma unroll
@@ -634,7 +642,7 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
       }
     }
 
-    mfma_priority(false);
+    mfma_priority(false, young);
     // ---- weights: exact step on a row tile's first key tile and on the tree tail, fast
     // step with the row-sum test elsewhere ----
     const bool masked = kt0 + KT > L;
@@ -686,7 +694,7 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
           (TV_LDS v4i16*)(vs + r1 * C::ROWB + ((chunk ^ swz_v<C::CH>(r1)) << 4) + half));
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    mfma_priority(true);
+    mfma_priority(true, young);
     constexpr int NV = DB * KS;                  // V operands per tile, db-major
     constexpr int PF = 1;                        // operands in flight ahead of the MFMAs
     bf16x8 va[PF + 1];
@@ -703,7 +711,7 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
                                                            o[t][db], 0, 0, 0);
       }
     }
-    mfma_priority(false);
+    mfma_priority(false, young);
   };
 
   // Tiles go in windows of WIN = NST/2: one barrier per window publishes its WIN tiles and
@@ -711,6 +719,9 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
   // while this one is computed.  The shared remainder tile of key tile `it` is computed by
   // wave it % NW, so within a window the extra work lands on WIN different waves.
   constexpr int WIN = NST / 2;
+  // The loop is compiled twice, for the older and the younger workgroup of a unit, so the
+  // priority switches inside the tiles take no branch.
+  auto key_loop = [&](auto young_c) {
   for (int it = 0; it < ntiles; it += WIN) {
     if (it == 0) {
       // the prologue issued tiles 0 .. min(NST, ntiles)-1; tiles of window 1 may remain
@@ -741,8 +752,18 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
 #pragma unroll
     for (int s = 0; s < WIN; ++s) {
       const int tt = it + s;
-      if (tt < ntiles) tile(tt, RR && (tt % NW) == w);
+      if (tt < ntiles) tile(tt, RR && (tt % NW) == w, young_c);
     }
+  }
+  };
+  if constexpr (NW == 4 && TN <= 2) {  // the shapes the host may flag (three-tile waves
+                                       // would spill with two copies of the loop)
+    if ((int)((blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) >= p.young_from)
+      key_loop(std::true_type{});
+    else
+      key_loop(std::false_type{});
+  } else {
+    key_loop(std::false_type{});
   }
 
   // ---- epilogue: full tiles straight from registers ----

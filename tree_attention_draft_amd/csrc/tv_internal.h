@@ -47,6 +47,8 @@ struct AttnParams {
   int32_t rope;        // fused rotary embedding of q and the tree keys at L + depth
   double rope_log2_theta;
   int32_t lpt;         // MFMA: workgroups take (request, chunk) pieces longest first (ragged)
+  int32_t young_from;  // MFMA: workgroups from this linear index on get the higher vector
+                       // issue priority (INT32_MAX: none)
   int32_t* meta_depth;     // optional [B, N] copies of the expanded tree (may be null)
   uint64_t* meta_bitmask;
   int32_t* meta_pos;
