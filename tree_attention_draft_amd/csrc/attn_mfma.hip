@@ -722,39 +722,39 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
   // The loop is compiled twice, for the older and the younger workgroup of a unit, so the
   // priority switches inside the tiles take no branch.
   auto key_loop = [&](auto young_c) {
-  for (int it = 0; it < ntiles; it += WIN) {
-    if (it == 0) {
-      // the prologue issued tiles 0 .. min(NST, ntiles)-1; tiles of window 1 may remain
-      wait_tiles<C::LPW, WIN>(min(ntiles, NST) - min(ntiles, WIN));
-    } else {
-      wait_vmcnt<0>();  // this window's tiles were the last ones issued
-    }
-    __syncthreads();  // window visible to all waves; the previous window's stages are free
-    if (it > 0) {
+    for (int it = 0; it < ntiles; it += WIN) {
+      if (it == 0) {
+        // the prologue issued tiles 0 .. min(NST, ntiles)-1; tiles of window 1 may remain
+        wait_tiles<C::LPW, WIN>(min(ntiles, NST) - min(ntiles, WIN));
+      } else {
+        wait_vmcnt<0>();  // this window's tiles were the last ones issued
+      }
+      __syncthreads();  // window visible to all waves; the previous window's stages are free
+      if (it > 0) {
+#pragma unroll
+        for (int s = 0; s < WIN; ++s) {
+          const int tn = it + WIN + s;
+          if (tn < ntiles)
+            issue_tile<C, NW, KT>(p, rm, lp, kg, vg, sbase + (tn % NST) * C::STAGEB,
+                                  kbeg + tn * KT, kend, fast, pfast, w, lane);
+        }
+      }
+      if (ROPE && kbeg + (it + WIN) * KT > L) {  // the window holds tree keys (uniform)
+        if constexpr (RR)
+          rope_tree_keys_outlined<C, KT, NST, WIN>(smem, it, ntiles, kbeg, kend, L, mask_s,
+                                                   inv_s, tid, NW * 64);
+        else
+          rope_tree_keys<C, KT, NST, WIN>(smem, it, ntiles, kbeg, kend, L, mask_s, inv_s, tid,
+                                          NW * 64);
+        __syncthreads();
+      }
+      if (!head_on) continue;  // surplus wave of a group smaller than NW: loads only
 #pragma unroll
       for (int s = 0; s < WIN; ++s) {
-        const int tn = it + WIN + s;
-        if (tn < ntiles)
-          issue_tile<C, NW, KT>(p, rm, lp, kg, vg, sbase + (tn % NST) * C::STAGEB,
-                                kbeg + tn * KT, kend, fast, pfast, w, lane);
+        const int tt = it + s;
+        if (tt < ntiles) tile(tt, RR && (tt % NW) == w, young_c);
       }
     }
-    if (ROPE && kbeg + (it + WIN) * KT > L) {  // the window holds tree keys (uniform)
-      if constexpr (RR)
-        rope_tree_keys_outlined<C, KT, NST, WIN>(smem, it, ntiles, kbeg, kend, L, mask_s,
-                                                 inv_s, tid, NW * 64);
-      else
-        rope_tree_keys<C, KT, NST, WIN>(smem, it, ntiles, kbeg, kend, L, mask_s, inv_s, tid,
-                                        NW * 64);
-      __syncthreads();
-    }
-    if (!head_on) continue;  // surplus wave of a group smaller than NW: loads only
-#pragma unroll
-    for (int s = 0; s < WIN; ++s) {
-      const int tt = it + s;
-      if (tt < ntiles) tile(tt, RR && (tt % NW) == w, young_c);
-    }
-  }
   };
   if constexpr (NW == 4 && TN <= 2) {  // the shapes the host may flag (three-tile waves
                                        // would spill with two copies of the loop)
