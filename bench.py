@@ -134,14 +134,9 @@ def bench_after_pass(args):
     am = logits.float().argmax(-1).cpu().numpy()
     tokens = rng.integers(0, V, size=(B, N)).astype(np.int32)
     for b in range(B):
-        node = 0
-        while True:
-            kids = [c for c in range(N) if parents[b][c] == node]
-            if not kids:
-                break
-            c = kids[int(rng.integers(0, len(kids)))]
-            tokens[b, c] = am[b, node]
-            node = c
+        path = workloads.random_root_path(rng, list(parents[b]))
+        for u, c in zip(path, path[1:]):
+            tokens[b, c] = am[b, u]
     tok = torch.from_numpy(tokens).to(dev)
     target = torch.empty((B, N), dtype=torch.int32, device=dev)
     acc = torch.empty((B, N), dtype=torch.int32, device=dev)

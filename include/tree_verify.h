@@ -102,8 +102,8 @@ tv_status tree_meta_build_batch(const int32_t* ranks, const int64_t* path_off,
 
 /*
  * tree_meta_from_parent -- the same metadata from device-resident parent arrays (the
- * parent-array form a kernel "expands per tile": "Tree attention mask for draft-tree
- * verification", paragraph after the build listing).
+ * faster kernel input is the parent array, expanded tile by tile inside the kernel: "Tree
+ * attention mask for draft-tree verification", paragraph after the build listing).
  *
  * Device memory: parent[b * parent_sb + i] (int32; parent_sb = 0 shares one tree across
  * the batch), prefix_len[b] (int32; may be NULL, then pos = depth).
@@ -323,10 +323,9 @@ typedef struct {
 
 /*
  * tree_kv_compact -- move the accepted path's KV rows to consecutive positions ("Tree
- * attention mask for draft-tree verification", "What it costs": node KV was written in
- * node order, so the accepted entries move to contiguous positions before the next step;
- * "Tree Verification", "The Cost Side": everything off the surviving path is rolled
- * back).  For every request and kv head, the K and V rows of accepted node a_j move from
+ * attention mask for draft-tree verification", "What it costs": the tree's cache rows sit
+ * in node order, and before the next step the accepted ones are packed together;
+ * "Tree Verification", "The Cost Side": cache rows of rejected branches are discarded).  For every request and kv head, the K and V rows of accepted node a_j move from
  * logical position L + a_j to L + j, j < A; rows at or past L + A are left as they are
  * (the new cache length excludes them).  All source rows of a (request, kv head) are read
  * before any is written, so overlapping moves are safe.  One workgroup per (kv head,
@@ -342,8 +341,8 @@ tv_status tree_kv_compact(const tv_compact_args* a, hipStream_t stream);
  * Acceptance model ("Tree attention mask for draft-tree verification", "What it buys"):
  * rank_prob[r] is the probability that the target's greedy token is the drafter's rank-r
  * candidate (each in [0, 1], sum <= 1, 1 <= num_ranks <= 4096; ranks >= num_ranks have
- * probability 0).  A node is reached with the product of its ranks' probabilities along
- * its path from the root.
+ * probability 0).  The probability of reaching a node is the product of rank_prob over
+ * the ranks on its path from the root.
  */
 
 /*

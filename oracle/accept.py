@@ -5,12 +5,13 @@ plain Python / numpy, sharing nothing with the HIP path.
 
 Sources:
   [TAM] "Tree attention mask for draft-tree verification" (inferenceinterviews.com),
-        "A strong answer" (the greedy walk and its tests) and "What it costs" (the
-        accepted entries are moved to contiguous positions before the next step).
+        "A strong answer" (the greedy walk and its tests) and "What it costs" (before
+        the next step the accepted nodes' cache entries are packed into consecutive
+        positions).
   [TV]  "Tree Verification" (stable-lab specdec notes), "Accepting on a Tree" (top-down
         walk, first matching child wins, a replacement token where the walk stops, a
-        bonus token at a leaf) and "The Cost Side" (everything off the surviving path is
-        rolled back).
+        bonus token at a leaf) and "The Cost Side" (cache entries of rejected branches
+        are discarded).
 
 Readings where the pages leave a step open (shared with the HIP path as written
 specification only):
@@ -29,52 +30,60 @@ from . import meta as _meta
 
 def argmax_rows(logits):
     """Target's greedy next token after every node: argmax over the last axis, lowest
-    index on ties, first NaN if a row holds one ([TAM] accept_greedy's target_argmax)."""
+    index on ties, first NaN if a row holds one ([TAM] "A strong answer": the walk
+    compares draft tokens with the target's greedy choices)."""
     x = np.asarray(logits, dtype=np.float64)
     return np.argmax(x, axis=-1).astype(np.int64)
 
 
-def children(parent, node):
-    """Children of ``node`` in node order."""
-    return [c for c in range(len(parent)) if parent[c] == node]
+def child_table(parent):
+    """For every node, the list of its children in ascending node order."""
+    table = [[] for _ in parent]
+    for c in range(1, len(parent)):
+        table[parent[c]].append(c)
+    return table
 
 
-def accept_greedy(parent, tokens, target_argmax):
+def accept_greedy(parent, draft, greedy_after):
     """Greedy walk ([TAM] "A strong answer"; [TV] "Accepting on a Tree").
+
+    ``draft[i]``: the draft token of node i (node 0's is never read); ``greedy_after[i]``:
+    the target's greedy token for the position after node i.
 
     Start at the root.  At the current node the target's greedy token is emitted; then
     the first child (in node order) whose draft token equals that greedy token is
     accepted and becomes the current node.  The walk stops when no child matches (the
     emitted token is then the correction) or the node is a leaf (the emitted token is
-    the bonus).
+    the bonus).  Every step goes one level deeper, so there are at most N steps.
 
     Returns (accepted node indices, root first; emitted tokens).  len(emitted) =
     len(accepted) and ranges over 1 .. depth + 1.
     """
     parent = [int(p) for p in parent]
     _meta.validate_parent(parent)
-    node, accepted, emitted = 0, [0], []
-    while True:
-        want = int(target_argmax[node])
-        emitted.append(want)
-        nxt = None
-        for c in children(parent, node):
-            if int(tokens[c]) == want:
-                nxt = c
-                break
-        if nxt is None:
-            return accepted, emitted
-        accepted.append(nxt)
-        node = nxt
+    table = child_table(parent)
+    accepted, emitted = [0], []
+    for _ in range(len(parent)):
+        here = accepted[-1]
+        greedy = int(greedy_after[here])
+        emitted.append(greedy)
+        matching = [c for c in table[here] if int(draft[c]) == greedy]
+        if not matching:
+            break
+        accepted.append(matching[0])
+    return accepted, emitted
 
 
 def is_root_path(parent, accepted):
-    """True when ``accepted`` starts at the root and each entry is a child of the one
-    before it."""
-    if len(accepted) == 0 or accepted[0] != 0:
+    """True when ``accepted`` is a root path of the tree: 1 <= len <= N, it starts at the
+    root, every entry is a node index, and each entry is a child of the one before it."""
+    n = len(parent)
+    if not 1 <= len(accepted) <= n or accepted[0] != 0:
         return False
-    return all(0 <= accepted[j] < len(parent) and parent[accepted[j]] == accepted[j - 1]
-               for j in range(1, len(accepted)))
+    for prev, cur in zip(accepted, accepted[1:]):
+        if not (0 <= cur < n) or parent[cur] != prev:
+            return False
+    return True
 
 
 def compact_request(k, v, prefix_len, accepted):

@@ -8,7 +8,7 @@ Definition followed:
 * Node i attends to every prefix position and to tree position L + j exactly when j is i
   or one of its ancestors; nothing else.  [TAM, "TL;DR"; TV, "Tree Attention"]
 * Tree node j's key/value sits at logical position L + j, in node order.  [TAM, "What it
-  costs": node KV is written in node order]
+  costs": the tree's cache rows sit in node order]
 * Under that mask one pass gives every node the same result a separate causal pass over
   its own root path would give.  [TV, "Tree Attention"; EBH]
 

@@ -3,9 +3,9 @@ Test infrastructure (see ``oracle/__init__``).
 
 The pages' correctness condition for tree verification is that node v's result equals
 what a separate, ordinary causal pass over (cached prefix, root path of v) produces.
-[TV, "Tree Attention" and "The Cost Side"; EBH: compare small-tree outputs against
-separate ordinary runs on each root-to-node path, with unequal branch lengths and
-repeated token labels]
+[TV, "Tree Attention" and "The Cost Side"; EBH: the recommended test checks a small
+tree against one ordinary pass per node, on trees whose branches differ in length and
+whose nodes reuse token labels]
 
 So for every node i this module builds the ordinary sequence
 

@@ -6,10 +6,11 @@ floats (IEEE double), sharing nothing with the library's host C++ code.
 
 Sources:
   [TAM] "Tree attention mask for draft-tree verification" (inferenceinterviews.com),
-        "What it buys" (a node is reached with the product of its ranks' probabilities;
-        expected tokens per step = 1 + the sum over nodes) and "What it costs" (B x N
-        tokens per step against the ridge of a bandwidth-bound decode step; break-even
-        batch = ridge / N; trees shrink toward a chain as the batch approaches the ridge).
+        "What it buys" (reach probability of a node = product of the probabilities of
+        the ranks on its path; expected tokens per step = 1 + the sum over nodes) and
+        "What it costs" (B x N tokens per step against the ridge of a bandwidth-bound
+        decode step; break-even batch = ridge / N; the tree narrows to a chain, then to
+        the root alone, as B x N nears the ridge).
   [TV]  "Tree Verification" (stable-lab specdec notes), "The Cost Side" (a node's expected
         contribution is its path product; spend the node budget where the acceptance mass
         is).

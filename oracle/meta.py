@@ -4,24 +4,31 @@ What is computed, and where the pages fix it:
 
 * A draft candidate is a tuple of drafter ranks; rank 0 is the top guess, so ``(0, 1)`` is
   the second guess for the token that follows the top guess.  Node 0 is the root, the
-  last accepted token.  [TAM, "A strong answer", the tree paragraph and build listing]
-* Distinct paths become nodes 1.. in (length, lexicographic) order.  A path whose
-  one-shorter prefix is neither the root nor another path is rejected.  The parent of a
-  node is the node of its one-shorter prefix; its depth is the path length (root 0).
-  [TAM, "A strong answer"; EBH: first proposed tokens have depth one]
-* Node i may attend to node j exactly when j is i or an ancestor of i -- never a
-  sibling branch.  [TAM, "A strong answer", the mask paragraph; TV, "Tree Attention"]
+  last accepted token, with the empty path.  [TAM, "A strong answer", the tree paragraph]
+* Distinct paths become nodes 1.. in (length, lexicographic) order.  A candidate whose
+  path minus its last rank is neither the root nor another candidate is rejected.  The
+  parent of a node is the node of that shortened path; its depth is the path length
+  (root 0).  [TAM, "A strong answer", build listing and tests paragraph; EBH: depth
+  counts from the root, whose children sit at depth 1]
+* A node sees another tree node only when that node is itself or lies on its own root
+  path; alternatives on other branches are never visible.  For rank paths this is the
+  prefix relation: node j is an ancestor-or-self of node i exactly when j's path is a
+  prefix of i's path.  [TAM, "A strong answer", the mask paragraph; TV, "Tree Attention"]
 * Position id = prefix length + depth, so siblings share a position.
   [TAM, "TL;DR" and the mask paragraph; TV, "Tree Attention"; EBH]
 * Any storage order in which a parent precedes its children is valid; the meaning comes
   from the parent array alone.  [TV, "Tree Attention"; EBH]
 
+Two derivations are kept on purpose, so that each checks the other: ``build_from_paths``
+takes the ancestor relation from the path-prefix relation, ``meta_from_parent`` from the
+parent array (a node's ancestor set is its parent's set plus itself).
+
 Readings where the pages are silent (each is also listed in the design notes):
 * an empty tuple or a negative rank is an invalid path (error "invalid_path");
 * on a missing parent the error names the offending path's index in the *input*
-  sequence (first occurrence), for the first such path in sorted order;
-* the bitmask of node i has bit j set (LSB-first, 64 bits per word) iff node j is i or an
-  ancestor of i; bits at or above N are zero.
+  sequence (first occurrence), for the first such path in node order;
+* the bitmask of node i has bit j set (LSB-first) iff node j is i or an ancestor of i;
+  bits at or above N are zero.
 """
 
 MAX_NODES = 64
@@ -50,39 +57,14 @@ def _canonical_path(p, k):
     return t
 
 
-def ancestors_or_self(parent, i):
-    """Node ids on the root path of node ``i``, from ``i`` up to the root, inclusive."""
-    out = []
-    j = i
-    while j != -1:
-        out.append(j)
-        j = parent[j]
-    return out
+def _is_prefix(a, b):
+    """True when rank tuple ``a`` is a prefix of rank tuple ``b`` (``a == b`` included)."""
+    return len(a) <= len(b) and b[:len(a)] == a
 
 
-def _bitmask_from_parent(parent):
-    masks = []
-    for i in range(len(parent)):
-        m = 0
-        for j in ancestors_or_self(parent, i):
-            m |= 1 << j
-        masks.append(m)
-    return masks
-
-
-def dense_mask(parent):
-    """N x N nested lists of bools: ``mask[i][j]`` is True iff j is i or an ancestor of i."""
-    n = len(parent)
-    rows = []
-    for i in range(n):
-        allowed = set(ancestors_or_self(parent, i))
-        rows.append([j in allowed for j in range(n)])
-    return rows
-
-
-def bitmask_words(mask_int, n_words=1):
-    """Split a Python-int bitmask into ``n_words`` unsigned 64-bit words, LSB first."""
-    return [(mask_int >> (64 * w)) & 0xFFFFFFFFFFFFFFFF for w in range(n_words)]
+def _bits(rows):
+    """Per row of a boolean matrix, the integer with bit j set where the row is True."""
+    return [sum(1 << j for j, on in enumerate(row) if on) for row in rows]
 
 
 def build_from_paths(paths, prefix_len, max_nodes=MAX_NODES):
@@ -92,33 +74,35 @@ def build_from_paths(paths, prefix_len, max_nodes=MAX_NODES):
     Python ints, one per node), ``mask`` (nested bool lists) and ``paths`` (the node order:
     ``paths[i]`` is node i's rank tuple, ``()`` for the root).  Raises :class:`TreeError`.
     """
-    first_index = {}
+    # distinct candidates, each remembered by the input index of its first occurrence
+    seen_at = {}
     for k, p in enumerate(paths):
-        t = _canonical_path(p, k)
-        if t not in first_index:
-            first_index[t] = k
-    ordered = sorted(first_index, key=lambda t: (len(t), t))
-    if len(ordered) + 1 > max_nodes:
-        raise TreeError("capacity", -1,
-                        f"{len(ordered) + 1} nodes exceed the capacity of {max_nodes}")
-    node_of = {(): 0}
+        seen_at.setdefault(_canonical_path(p, k), k)
+    nodes = [()] + sorted(seen_at, key=lambda t: (len(t), t))
+    n = len(nodes)
+    if n > max_nodes:
+        raise TreeError("capacity", -1, f"{n} nodes exceed the capacity of {max_nodes}")
+
+    # parent: the node whose path is this path minus its last rank (searched for)
     parent = [-1]
-    depth = [0]
-    for t in ordered:
-        up = t[:-1]
-        if up not in node_of:
-            raise TreeError("missing_parent", first_index[t],
-                            f"path {t} (input index {first_index[t]}) has no parent {up}")
-        node_of[t] = len(parent)
-        parent.append(node_of[up])
-        depth.append(len(t))
+    for i in range(1, n):
+        shorter = nodes[i][:-1]
+        hits = [j for j in range(n) if nodes[j] == shorter]
+        if not hits:
+            raise TreeError("missing_parent", seen_at[nodes[i]],
+                            f"path {nodes[i]} (input index {seen_at[nodes[i]]}) has no "
+                            f"parent {shorter}")
+        parent.append(hits[0])
+
+    depth = [len(t) for t in nodes]
+    mask = [[_is_prefix(nodes[j], nodes[i]) for j in range(n)] for i in range(n)]
     return {
         "parent": parent,
         "depth": depth,
         "pos": [prefix_len + d for d in depth],
-        "bitmask": _bitmask_from_parent(parent),
-        "mask": dense_mask(parent),
-        "paths": [()] + ordered,
+        "bitmask": _bits(mask),
+        "mask": mask,
+        "paths": nodes,
     }
 
 
@@ -136,15 +120,37 @@ def validate_parent(parent):
                             f"node {i} has parent {parent[i]}; need 0 <= parent < {i}")
 
 
+def ancestor_sets(parent):
+    """Ancestor-or-self set of every node of a parent-before-child array: the root's is
+    {0}; any other node's is its parent's set plus itself (the parent comes first, so its
+    set is already known)."""
+    sets = []
+    for i, p in enumerate(parent):
+        sets.append({i} if p < 0 else sets[p] | {i})
+    return sets
+
+
+def dense_mask(parent):
+    """N x N nested lists of bools: ``mask[i][j]`` is True iff j is i or an ancestor of i."""
+    parent = [int(x) for x in parent]
+    validate_parent(parent)
+    sets = ancestor_sets(parent)
+    n = len(parent)
+    return [[j in sets[i] for j in range(n)] for i in range(n)]
+
+
 def meta_from_parent(parent, prefix_len):
     """Parent array (parent-before-child order) -> depth, bitmask, pos, mask."""
     parent = [int(x) for x in parent]
     validate_parent(parent)
-    depth = [len(ancestors_or_self(parent, i)) - 1 for i in range(len(parent))]
+    depth = [0] * len(parent)
+    for i in range(1, len(parent)):
+        depth[i] = depth[parent[i]] + 1
+    mask = dense_mask(parent)
     return {
         "parent": parent,
         "depth": depth,
         "pos": [prefix_len + d for d in depth],
-        "bitmask": _bitmask_from_parent(parent),
-        "mask": dense_mask(parent),
+        "bitmask": _bits(mask),
+        "mask": mask,
     }

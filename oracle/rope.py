@@ -5,10 +5,10 @@ numpy float64, sharing nothing with the HIP path.
 Sources:
   [TAM] "Tree attention mask for draft-tree verification" (inferenceinterviews.com),
         "What interviewers probe next" (siblings share a position: rotary embedding must
-        rotate a node as if it sat at its own depth) and "Common mistakes" (sequential
-        position ids for the flattened tree break rotary embeddings); "What it costs"
-        (tree KV is written in node order and the accepted entries move to contiguous
-        positions).
+        rotate a node as if it sat at its own depth) and "Common mistakes" (numbering the
+        flattened nodes 0, 1, 2, ... as positions breaks rotary embeddings); "What it
+        costs" (the tree's cache rows sit in node order; the accepted ones are packed
+        together afterwards).
   [EBH] "Encode branch histories in masks and positions": positional features follow the
         model's position semantics (depth), not the flattened storage order.
 

@@ -21,8 +21,7 @@ def test_expected_tokens_random_trees(seed):
     for n in (1, 2, 10, 33, 64):
         paths, _ = workloads.random_tree(rng, n, 8)
         b = om.build_from_paths(paths, 0)
-        order = sorted(set(tuple(p) for p in paths), key=lambda p: (len(p), p))
-        rank = [0] + [p[-1] for p in order]
+        rank = [0] + [p[-1] for p in b["paths"][1:]]
         probs = random_probs(rng, int(rng.integers(1, 6)))
         e, reach = tv.tree_expected_tokens(b["parent"], rank, probs)
         assert abs(e - ob.expected_tokens(b["parent"], rank, probs)) < 1e-12

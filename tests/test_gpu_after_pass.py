@@ -92,14 +92,9 @@ def test_walk_goes_deep_with_matching_logits():
     # the target agrees with the draft along one random root-to-leaf path per request
     x = rng.standard_normal((B, N, V)).astype(np.float32)
     for b in range(B):
-        node = 0
-        while True:
-            kids = [c for c in range(N) if parents[b][c] == node]
-            if not kids:
-                break
-            c = kids[int(rng.integers(0, len(kids)))]
-            x[b, node, tokens[b][c]] = 50.0
-            node = c
+        path = workloads.random_root_path(rng, list(parents[b]))
+        for u, c in zip(path, path[1:]):
+            x[b, u, tokens[b][c]] = 50.0
     logits = to_dev(x, "f32")
     target, acc, em, na = tv.tree_accept_greedy(
         logits, torch.tensor(np.array(tokens, np.int32)).cuda(),

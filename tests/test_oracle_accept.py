@@ -3,8 +3,9 @@
 ``oracle.accept`` is pinned against things other than itself:
 * the walks the worked example's tests name ([TAM] "A strong answer"): one that takes the
   second-rank branch (it accepts nodes 0, 2, 5 -- the nodes [TAM] "What it costs" then
-  compacts), one that reaches the deepest leaf and emits all four drafts plus the bonus,
-  the empty tree (one token) and a rejection at the root (one correction token);
+  compacts), one that goes down to the deepest leaf (four accepted drafts, then the
+  bonus), the empty tree (one token) and a rejection at the root (one correction token);
+* ``is_root_path`` against hand-made lists that break each of its conditions;
 * the expected tokens per step the page prints (3.28 for the tree, 2.77 for the chain of
   four), recomputed by exact enumeration of every greedy outcome of the rank-acceptance
   model through the walk;
@@ -38,7 +39,7 @@ def tree10():
 
 def rank_tokens(paths):
     """Draft token of each node = its rank among its siblings (node 0: unused -1)."""
-    return [-1] + [p[-1] for p in sorted(set(paths), key=lambda p: (len(p), p))]
+    return [-1] + [p[-1] for p in meta.build_from_paths(paths, 0)["paths"][1:]]
 
 
 # ------------------------------------------------------------- the page's walks -----
@@ -148,6 +149,24 @@ def test_walk_matches_per_node_rule(seed):
         assert accept.is_root_path(parent, got[0])
 
 
+@pytest.mark.parametrize("lst,ok", [
+    ([0], True), ([0, 2, 5], True), ([0, 1, 3, 6, 9], True),
+    ([], False),                    # empty
+    ([2, 5], False),                # does not start at the root
+    ([1], False),                   # a single entry that is not the root
+    ([0, 3], False),                # 3 is a grandchild of the root, not a child
+    ([0, 1, 2], False),             # 2 is 1's sibling, not its child
+    ([0, 10], False),               # out of range (N = 10)
+    ([0, -1], False),               # negative entry
+    ([0, 1, 3, 6, 9, 9], False),    # repeats the leaf: not a child of itself
+    ([0, 2, 5, 5, 5, 5, 5, 5, 5, 5, 5], False),  # longer than N
+    ([0, 0], False),                # the root again
+])
+def test_is_root_path_against_hand_made_lists(lst, ok):
+    _, _, parent = tree10()         # parent = -1,0,0,1,1,2,3,3,4,6
+    assert accept.is_root_path(parent, lst) is ok
+
+
 def test_argmax_rows_ties_and_nan():
     x = np.array([[1.0, 3.0, 3.0, 2.0], [np.nan, 5.0, np.nan, 1.0], [-1.0, -1.0, -1.0, -1.0]])
     assert accept.argmax_rows(x).tolist() == [1, 0, 0]
@@ -160,14 +179,15 @@ def test_planted_mistakes_fail():
     am = [1, 9, 0, 9, 9, 7, 9, 9, 9, 9]
 
     def walk_last_match(parent, tokens, target):     # takes the LAST matching child
-        node, acc, em = 0, [0], []
-        while True:
-            em.append(target[node])
-            kids = [c for c in accept.children(parent, node) if tokens[c] == target[node]]
-            if not kids:
-                return acc, em
-            acc.append(kids[-1])
-            node = kids[-1]
+        table = accept.child_table(parent)
+        acc, em = [0], []
+        for _ in range(len(parent)):
+            em.append(target[acc[-1]])
+            hit = [c for c in table[acc[-1]] if tokens[c] == target[acc[-1]]]
+            if not hit:
+                break
+            acc.append(hit[-1])
+        return acc, em
 
     def walk_no_bonus(parent, tokens, target):       # forgets the final token
         acc, em = accept.accept_greedy(parent, tokens, target)

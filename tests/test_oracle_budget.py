@@ -30,8 +30,7 @@ PAGE_PROBS = [0.7, 0.15]
 def ranked(paths):
     """(parent, rank) of the tree the builder makes from rank paths."""
     b = meta.build_from_paths(paths, 0)
-    order = sorted(set(tuple(p) for p in paths), key=lambda p: (len(p), p))
-    return b["parent"], [0] + [p[-1] for p in order]
+    return b["parent"], [0] + [p[-1] for p in b["paths"][1:]]
 
 
 def page_tree():

@@ -3,8 +3,8 @@
 //
 // Method ("Tree attention mask for draft-tree verification", sections "What it buys" and
 // "What it costs"; "Tree Verification", section "The Cost Side"): under greedy
-// verification a node is reached with the product of its drafter ranks' acceptance
-// probabilities along its path, and the expected tokens per step are one (the target's own
+// verification the chance of reaching a node is the product, over the drafter ranks on
+// its path, of each rank's acceptance probability, and the expected tokens per step are one (the target's own
 // token) plus the sum of those products.  A step verifies B x N tokens; below the ridge of
 // a bandwidth-bound decode step that costs about one pass, past it every extra node is
 // paid-for compute, so the tree shrinks as the batch grows.  A node's worth is its path

@@ -59,6 +59,23 @@ def random_tree(rng, n_nodes, depth_cap):
     return paths[1:], creation_parent
 
 
+def random_root_path(rng, parent):
+    """Nodes from the root down to a leaf picked uniformly at random (an input for tests
+    that want draft tokens agreeing with the target along one branch).  The leaf's
+    ancestors are collected by climbing its parent links."""
+    n = len(parent)
+    has_child = [False] * n
+    for c in range(1, n):
+        has_child[parent[c]] = True
+    leaves = [i for i in range(n) if not has_child[i]]
+    node = leaves[int(rng.integers(len(leaves)))]
+    up = []
+    while node >= 0:
+        up.append(node)
+        node = parent[node]
+    return up[::-1]
+
+
 def normal_f32(rng, shape):
     return rng.standard_normal(size=shape, dtype=np.float32)
 
