@@ -15,7 +15,8 @@
  *    is safe to capture in a HIP graph (sizes come from arguments, never from constants).
  *  - Errors are returned as tv_status; a human-readable detail of the last error on the
  *    calling thread is available from tv_last_error().  Nothing is written to outputs when
- *    an argument check fails.
+ *    an argument check fails.  N > TV_MAX_NODES (or D outside {64, 128}) is a shape the
+ *    kernels do not implement: TV_ERR_UNSUPPORTED; N < 1 is TV_ERR_INVALID_ARG.
  *  - N (nodes per tree, root included) is 1..TV_MAX_NODES.  The ancestor bitmask of node i
  *    is one uint64 word with bit j set (LSB first) iff j is i or an ancestor of i.
  *  - Device-resident parent arrays must satisfy parent[0] == -1 and 0 <= parent[i] < i
@@ -89,9 +90,14 @@ tv_status tree_meta_build(const int32_t* ranks, const int64_t* path_off, int32_t
  * num_nodes[b] = the tree's own node count.  A tree with fewer than N nodes is padded with
  * extra leaves under the root (parent 0) so that the row still satisfies the parent
  * convention; callers ignore outputs of nodes at or past num_nodes[b].
- * Errors: as tree_meta_build for the first failing tree; *bad_tree names it (may be NULL)
- * and *bad_path the offending path's index within that tree.  TV_ERR_CAPACITY when a tree
- * has more than N nodes.
+ * Errors: TV_ERR_INVALID_ARG (B < 0, N < 1, null pointers, tree_off or path_off not
+ * starting at 0 or decreasing, a prefix length out of range -- *bad_tree names that tree)
+ * and TV_ERR_UNSUPPORTED (N > TV_MAX_NODES): these checks cover the whole batch before
+ * anything is written.  Then, per tree in order, the errors of tree_meta_build
+ * (TV_ERR_INVALID_PATH, TV_ERR_MISSING_PARENT, TV_ERR_CAPACITY when a tree has more than
+ * N nodes): *bad_tree names the first failing tree (may be NULL) and *bad_path the
+ * offending path's index within it; rows of the trees before it hold their results, the
+ * rest of the outputs are unspecified.  B == 0 is a no-op.
  */
 tv_status tree_meta_build_batch(const int32_t* ranks, const int64_t* path_off,
                                 const int64_t* tree_off, int32_t B,
@@ -109,8 +115,8 @@ tv_status tree_meta_build_batch(const int32_t* ranks, const int64_t* path_off,
  * the batch), prefix_len[b] (int32; may be NULL, then pos = depth).
  * Device outputs, dense [B, N]: depth (int32), bitmask (uint64), pos (int32); any of the
  * three may be NULL to skip it.  Invalid nodes (see header comment) get -1 / 0 / -1.
- * Errors: TV_ERR_INVALID_ARG (B < 0, N outside 1..64, parent NULL, parent_sb < 0),
- *         TV_ERR_HIP.  B == 0 is a no-op.
+ * Errors: TV_ERR_INVALID_ARG (B < 0, N < 1, parent NULL, parent_sb < 0),
+ *         TV_ERR_UNSUPPORTED (N > 64), TV_ERR_HIP.  B == 0 is a no-op.
  */
 tv_status tree_meta_from_parent(const int32_t* parent, int32_t parent_sb, int32_t B,
                                 int32_t N, const int32_t* prefix_len, int32_t* depth,

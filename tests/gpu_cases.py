@@ -126,3 +126,91 @@ class Case:
             assert eo <= tol and el <= tol, (self.name, b, eo, el)
         say(self.name, f"max_abs_err={worst:.3e} over requests {list(reqs)[:8]}")
         return worst
+
+
+class StreamedPagedCase(Case):
+    """A paged batch too large to hold on the host (long context at large batch): every
+    request's K and V are drawn with ``workloads.request_tensors`` (the same per-request
+    streams ``workloads.build_batch`` uses, so values match a host-built batch of the same
+    seeds) and copied into a NaN-filled device pool page by page, one request at a time.
+    The oracle regenerates a sampled request's tensors on the host from the same seed."""
+
+    def __init__(self, name, prefix_lens, trees, Hq=32, Hkv=8, D=128, seed=1000,
+                 page_size=16, page_seed=3000):
+        import concurrent.futures
+        import os
+        import torch
+        self.name = name
+        self.L = np.asarray(prefix_lens, np.int32)
+        self.B = len(self.L)
+        self.Hq, self.Hkv, self.D, self.dtype = Hq, Hkv, D, "bf16"
+        self.parent_gpu = [tv.tree_meta_build(t, 0)["parent"].tolist() for t in trees]
+        self.parent_oracle = [ometa.build_from_paths(t, 0)["parent"] for t in trees]
+        self.N = len(self.parent_gpu[0])
+        self.page_size = page_size
+        self.sm_scale = None
+        self.rope_theta = 0.0
+        self.seed = seed
+        S = int(self.L.max()) + self.N
+        prng = np.random.Generator(np.random.PCG64(page_seed))
+        table, n_pages = workloads.page_table(prng, self.B, S, page_size)
+        say(name, f"B={self.B} N={self.N} streamed paged pool {n_pages} pages "
+            f"({2 * n_pages * page_size * Hkv * D * 2 / 1e9:.1f} GB K+V) seed={seed}")
+        nan = torch.tensor(workloads.BF16_NAN_BITS, dtype=torch.int16).view(torch.bfloat16)
+        kpool = torch.full((n_pages, page_size, Hkv, D), float(nan.float()),
+                           dtype=torch.bfloat16, device="cuda")
+        vpool = torch.full_like(kpool, float(nan.float()))
+        q = np.empty((self.B, self.N, Hq, D), np.uint16)
+
+        def draw(b):
+            Lb = int(self.L[b])
+            qb, kb, vb = workloads.request_tensors(seed, b, self.N, Lb, Hq, Hkv, D)
+            T = Lb + self.N
+            npg = -(-T // page_size)
+            blocks = []
+            for x in (kb, vb):
+                pad = np.full((npg * page_size, Hkv, D), workloads.BF16_NAN_BITS, np.uint16)
+                pad[:T] = workloads.encode(x, "bf16")
+                blocks.append(pad.reshape(npg, page_size, Hkv, D))
+            return b, workloads.encode(qb, "bf16"), blocks, npg
+
+        def upload(result):
+            b, qb, (kblk, vblk), npg = result
+            q[b] = qb
+            idx = torch.from_numpy(table[b, :npg].astype(np.int64)).cuda()
+            for pool, blk in ((kpool, kblk), (vpool, vblk)):
+                src = torch.from_numpy(blk.view(np.int16)).view(torch.bfloat16).cuda()
+                pool.index_copy_(0, idx, src)
+            if b % 16 == 15:
+                say(name, f"uploaded {b + 1}/{self.B} requests")
+
+        # at most 2 x workers requests are held on the host at any time
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+            pending = []
+            for b in range(self.B):
+                pending.append(ex.submit(draw, b))
+                if len(pending) >= 2 * workers:
+                    upload(pending.pop(0).result())
+            for f in pending:
+                upload(f.result())
+        torch.cuda.synchronize()
+        self.host = {"q": q, "page_table": table}
+        self._dev = {"q": torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).cuda(),
+                     "k": kpool, "v": vpool,
+                     "prefix_len": torch.from_numpy(self.L).cuda(),
+                     "parent": torch.tensor(np.array(self.parent_gpu, np.int32)).cuda(),
+                     "page_table": torch.from_numpy(table).cuda()}
+
+    def request_inputs(self, b):
+        Lb = int(self.L[b])
+        qb, kb, vb = workloads.request_tensors(self.seed, b, self.N, Lb, self.Hq, self.Hkv,
+                                               self.D)
+        dec = oattn.bf16_bits_to_f64
+        return (dec(workloads.encode(qb, "bf16")), dec(workloads.encode(kb, "bf16")),
+                dec(workloads.encode(vb, "bf16")))
+
+    def release(self):
+        self._dev = None
+        import torch
+        torch.cuda.empty_cache()

@@ -208,7 +208,7 @@ def base_args(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(N=0), 1), (dict(N=65), 1), (dict(Hq=30), 1), (dict(Hkv=0), 1),
+    (dict(N=0), 1), (dict(N=65), 5), (dict(Hq=30), 1), (dict(Hkv=0), 1),
     (dict(D=96), 5), (dict(dtype=7), 1), (dict(B=-1), 1), (dict(q=None), 1),
     (dict(parent=None), 1), (dict(prefix_len=None), 1), (dict(out=None), 1),
     (dict(q_sn=100), 1), (dict(kv_st=-8), 1), (dict(k=(1 << 20) + 8), 1),
@@ -301,7 +301,7 @@ def test_single_split_needs_no_workspace():
 def test_meta_from_parent_argument_checks():
     L = tv.lib()
     assert L.tree_meta_from_parent(1 << 20, 0, 4, 0, None, None, None, None, None) == 1
-    assert L.tree_meta_from_parent(1 << 20, 0, 4, 65, None, None, None, None, None) == 1
+    assert L.tree_meta_from_parent(1 << 20, 0, 4, 65, None, None, None, None, None) == 5
     assert L.tree_meta_from_parent(1 << 20, 5, 4, 10, None, None, None, None, None) == 1
     assert L.tree_meta_from_parent(None, 0, 4, 10, None, None, None, None, None) == 1
     assert L.tree_meta_from_parent(None, 0, 0, 10, None, None, None, None, None) == 0
@@ -322,8 +322,13 @@ def base_accept_args(**kw):
     return a
 
 
+def test_accept_rejects_trees_above_64_nodes_as_unsupported():
+    L = tv.lib()
+    assert L.tree_accept_greedy(ctypes.byref(base_accept_args(N=65)), None) == 5
+
+
 @pytest.mark.parametrize("kw", [
-    dict(N=0), dict(N=65), dict(V=0), dict(B=-1), dict(dtype=5), dict(logits=None),
+    dict(N=0), dict(V=0), dict(B=-1), dict(dtype=5), dict(logits=None),
     dict(tokens=None), dict(parent=None), dict(target=None), dict(accepted=None),
     dict(emitted=None), dict(num_accepted=None), dict(lg_sn=999), dict(lg_sb=5000),
     dict(tokens_sb=3), dict(parent_sb=9), dict(logits=(1 << 20) + 1),
@@ -369,7 +374,7 @@ def base_compact_args(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(N=0), 1), (dict(N=65), 1), (dict(Hkv=0), 1), (dict(D=96), 5), (dict(B=-1), 1),
+    (dict(N=0), 1), (dict(N=65), 5), (dict(Hkv=0), 1), (dict(D=96), 5), (dict(B=-1), 1),
     (dict(dtype=4), 1), (dict(kv_layout=2), 1), (dict(k=None), 1), (dict(v=None), 1),
     (dict(prefix_len=None), 1), (dict(parent=None), 1), (dict(accepted=None), 1),
     (dict(num_accepted=None), 1), (dict(kv_st=-8), 1), (dict(kv_sh=4), 1),

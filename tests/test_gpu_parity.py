@@ -13,7 +13,7 @@ import tree_attention_draft_amd as tv  # noqa: E402
 from oracle import meta as ometa  # noqa: E402
 from tree_attention_draft_amd import workloads  # noqa: E402
 
-from gpu_cases import Case, say  # noqa: E402
+from gpu_cases import Case, StreamedPagedCase, say  # noqa: E402
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -415,6 +415,79 @@ def test_long_context_paged_sampled(B):
     c = Case(f"long_paged_B{B}", L, trees=trees, seed=1005, page_size=16, page_seed=3005)
     out, lse = _run_as_benchmark(c)
     c.check(out, lse, requests=_sampled(B)[:3])
+
+
+@pytest.mark.parametrize("B", [2, 4, 8, 32, 64, 128])
+def test_long_context_paged_batch_sweep(B):
+    # the rest of the long-context sweep (batch 1..128): pools of up to 17 GB are filled
+    # on the device request by request; the same seeds as the host-built B = 1, 16 cases
+    spec = workloads.WORKLOADS["long_paged_n33"]
+    trees, _ = workloads.trees_for(spec, batch=B)
+    L = workloads.prefix_lengths(spec, batch=B)
+    c = StreamedPagedCase(f"long_paged_sweep_B{B}", L, trees, seed=1005, page_size=16,
+                          page_seed=3005)
+    out, lse = _run_as_benchmark(c)
+    rng = np.random.Generator(np.random.PCG64(7000 + B))
+    extra = [int(x) for x in rng.choice(B, size=min(B, 2), replace=False)]
+    c.check(out, lse, requests=sorted(set(_sampled(B)[:3] + extra)))
+    c.release()
+
+
+def test_streamed_case_matches_host_built_batch():
+    # the streamed construction draws exactly the values of the host-built batch
+    spec = workloads.WORKLOADS["long_paged_n33"]
+    trees, _ = workloads.trees_for(spec, batch=2)
+    L = np.array([300, 1000], np.int32)
+    a = StreamedPagedCase("streamed_vs_host_s", L, trees, seed=1005, page_size=16,
+                          page_seed=3005)
+    b = Case("streamed_vs_host_h", L, trees=trees, seed=1005, page_size=16, page_seed=3005)
+    db = b.device()
+    assert np.array_equal(a.host["page_table"], b.host["page_table"])
+    for key in ("q", "k", "v"):
+        assert torch.equal(a.device()[key].view(torch.int16), db[key].view(torch.int16)), key
+    out_a, lse_a = a.run()
+    out_b, lse_b = b.run()
+    assert np.array_equal(out_a, out_b) and np.array_equal(lse_a, lse_b)
+
+
+def test_full_size_through_the_batched_builder():
+    # the benchmark's step: the library's batched builder writes the parent rows straight
+    # into pinned host memory, the pass reads them in place and exports the metadata
+    spec = workloads.WORKLOADS["b64_l4096_n33"]
+    trees, _ = workloads.trees_for(spec)
+    L = workloads.prefix_lengths(spec)
+    c = Case("b64_batched_builder", L, trees=trees, seed=1000 + spec["k"])
+    pinned = torch.empty((c.B, c.N), dtype=torch.int32).pin_memory()
+    built = tv.tree_meta_build_batch(tv.PackedTrees(trees), L, c.N, parent=pinned.numpy())
+    assert (built["num_nodes"] == c.N).all()
+    meta = _meta_outputs(c.B, c.N)
+    out, lse = c.run(parent=pinned, prefix_len_host=c.L, meta=meta)
+    _assert_meta(meta, _meta_ref(c.parent_oracle, c.L))
+    rng = np.random.Generator(np.random.PCG64(7100))
+    reqs = sorted(set(_sampled(c.B) + [int(x) for x in rng.choice(c.B, 3, replace=False)]))
+    c.check(out, lse, requests=reqs)
+
+
+def test_split_pass_on_a_side_stream():
+    # buffers the binding creates (outputs, split workspace) are allocated on the launch
+    # stream, so a pass enqueued on a non-current stream is not overwritten by later work
+    # on the current stream
+    paths, _ = random_trees(2700, 4, 33, 8)
+    c = Case("side_stream", [3000, 1500, 64, 2500], trees=paths, seed=2701)
+    ref_out, ref_lse = c.run(num_splits=5)
+    d = c.device()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        out, lse = tv.tree_verify_attn(d["q"], d["k"], d["v"], d["parent"], d["prefix_len"],
+                                       3000, num_splits=5, stream=side)
+        # scribble on fresh memory on the current stream meanwhile
+        junk = torch.full((64 << 20,), 7, dtype=torch.uint8, device="cuda")
+        del junk
+        side.synchronize()
+        assert np.array_equal(out.float().cpu().numpy(), ref_out)
+        assert np.array_equal(lse.cpu().numpy(), ref_lse)
+    torch.cuda.current_stream().wait_stream(side)
 
 
 @pytest.mark.parametrize("page_size", [1, 8, 12, 32, 64, 256])

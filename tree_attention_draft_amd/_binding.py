@@ -33,10 +33,11 @@ EXPORTS = ["tree_meta_build", "tree_meta_build_batch", "tree_meta_from_parent",
 
 
 class TreeVerifyError(RuntimeError):
-    def __init__(self, status, detail, bad_path=-1):
+    def __init__(self, status, detail, bad_path=-1, bad_tree=-1):
         self.status = status
         self.name = STATUS_NAMES.get(status, str(status))
         self.bad_path = bad_path
+        self.bad_tree = bad_tree
         super().__init__(f"{self.name}: {detail}" + (
             f" (input path {bad_path})" if bad_path >= 0 else ""))
 
@@ -222,7 +223,7 @@ def tree_meta_build_batch(packed, prefix_len, N, parent=None, depth=None, bitmas
         ctypes.byref(bp))
     if st != TV_OK:
         raise TreeVerifyError(st, lib().tv_last_error().decode() + f" (tree {bt.value})",
-                              bp.value)
+                              bp.value, bt.value)
     return {"parent": parent, "depth": depth, "bitmask": bitmask, "pos": pos,
             "num_nodes": nn}
 
@@ -233,10 +234,22 @@ def _torch():
     return torch
 
 
-def _stream(stream):
+def _torch_stream(stream):
+    """The torch stream the kernels are enqueued on: ``stream``, else the current one."""
     torch = _torch()
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    return torch.cuda.current_stream() if stream is None else stream
+
+
+def _stream(stream):
+    return ctypes.c_void_p(_torch_stream(stream).cuda_stream)
+
+
+def _on(stream):
+    """Context in which buffers this module creates are allocated on the launch stream.
+    The caching allocator then hands such a buffer to other work only in that stream's
+    order, i.e. after the kernels that write it -- also for the split workspace, which is
+    dropped when the call returns while its kernels may still be running."""
+    return _torch().cuda.stream(_torch_stream(stream))
 
 
 def _require_cuda(*tensors):
@@ -277,9 +290,11 @@ def tree_meta_from_parent(parent, prefix_len=None, batch=None, depth=None, bitma
         if parent.stride(1) != 1:
             raise ValueError("parent rows must be contiguous")
     dev = parent.device
-    depth = torch.empty((B, N), dtype=torch.int32, device=dev) if depth is None else depth
-    bitmask = torch.empty((B, N), dtype=torch.int64, device=dev) if bitmask is None else bitmask
-    pos = torch.empty((B, N), dtype=torch.int32, device=dev) if pos is None else pos
+    with _on(stream):
+        depth = torch.empty((B, N), dtype=torch.int32, device=dev) if depth is None else depth
+        bitmask = (torch.empty((B, N), dtype=torch.int64, device=dev) if bitmask is None
+                   else bitmask)
+        pos = torch.empty((B, N), dtype=torch.int32, device=dev) if pos is None else pos
     st = lib().tree_meta_from_parent(
         parent.data_ptr(), psb, B, N,
         prefix_len.data_ptr() if prefix_len is not None else None,
@@ -378,17 +393,19 @@ def tree_verify_attn(q, k, v, parent, prefix_len, max_prefix_len, *, page_table=
                                   or not t.is_contiguous()):
                 raise ValueError("meta outputs must be contiguous [B, N] int32/int64/int32")
     B, N, Hq, D = q.shape
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, N, Hq), dtype=torch.float32, device=q.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((B, N, Hq), dtype=torch.float32, device=q.device)
     a = make_args(q, k, v, parent, prefix_len, max_prefix_len, page_table=page_table,
                   page_size=page_size, sm_scale=sm_scale, out=out, lse=lse,
                   workspace=workspace, num_splits=num_splits, path=path,
                   rope_theta=rope_theta, prefix_len_host=prefix_len_host, meta=meta)
     need = int(lib().tree_verify_attn_workspace_size(ctypes.byref(a)))
     if need > 0 and (workspace is None or a.workspace_bytes < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        with _on(stream):
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         a.workspace = workspace.data_ptr()
         a.workspace_bytes = need
     st = lib().tree_verify_attn(ctypes.byref(a), _stream(stream))
@@ -461,12 +478,14 @@ def tree_accept_greedy(logits, tokens, parent, target=None, accepted=None, emitt
     dev = logits.device
     def mk(t, shape):
         return torch.empty(shape, dtype=torch.int32, device=dev) if t is None else t
-    target, accepted = mk(target, (B, N)), mk(accepted, (B, N))
-    emitted, num_accepted = mk(emitted, (B, N)), mk(num_accepted, (B,))
+    with _on(stream):
+        target, accepted = mk(target, (B, N)), mk(accepted, (B, N))
+        emitted, num_accepted = mk(emitted, (B, N)), mk(num_accepted, (B,))
     a = make_accept_args(logits, tokens, parent, target, accepted, emitted, num_accepted)
     need = int(lib().tree_accept_greedy_workspace_size(ctypes.byref(a)))
     if workspace is None or workspace.numel() * workspace.element_size() < need:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        with _on(stream):
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     a.workspace = workspace.data_ptr()
     a.workspace_bytes = workspace.numel() * workspace.element_size()
     _check(lib().tree_accept_greedy(ctypes.byref(a), _stream(stream)))
@@ -524,8 +543,9 @@ def tree_kv_compact(k, v, prefix_len, max_prefix_len, parent, accepted, num_acce
     _require_cuda(k, v, prefix_len, parent, accepted, num_accepted, page_table, new_len, status)
     B = prefix_len.shape[0]
     dev = k.device
-    new_len = torch.empty(B, dtype=torch.int32, device=dev) if new_len is None else new_len
-    status = torch.empty(B, dtype=torch.int32, device=dev) if status is None else status
+    with _on(stream):
+        new_len = torch.empty(B, dtype=torch.int32, device=dev) if new_len is None else new_len
+        status = torch.empty(B, dtype=torch.int32, device=dev) if status is None else status
     a = make_compact_args(k, v, prefix_len, max_prefix_len, parent, accepted, num_accepted,
                           page_table, page_size, new_len, status, rope_theta)
     _check(lib().tree_kv_compact(ctypes.byref(a), _stream(stream)))

@@ -77,7 +77,8 @@ tv_status check_args(const tv_attn_args* a, bool pointers) {
   if (!a) return fail(TV_ERR_INVALID_ARG, "args is null");
   if (a->dtype != TV_BF16 && a->dtype != TV_F32) return fail(TV_ERR_INVALID_ARG, "bad dtype");
   if (a->B < 0) return fail(TV_ERR_INVALID_ARG, "B < 0");
-  if (a->N < 1 || a->N > TV_MAX_NODES) return fail(TV_ERR_INVALID_ARG, "N outside 1..64");
+  if (a->N < 1) return fail(TV_ERR_INVALID_ARG, "N < 1");
+  if (a->N > TV_MAX_NODES) return fail(TV_ERR_UNSUPPORTED, "N > 64");
   if (a->Hq < 1 || a->Hkv < 1 || a->Hq % a->Hkv != 0)
     return fail(TV_ERR_INVALID_ARG, "need Hq >= 1, Hkv >= 1 and Hq % Hkv == 0");
   if (a->D != 64 && a->D != 128) return fail(TV_ERR_UNSUPPORTED, "D must be 64 or 128");
@@ -312,7 +313,8 @@ extern "C" tv_status tree_meta_from_parent(const int32_t* parent, int32_t parent
                                            int32_t* depth, uint64_t* bitmask, int32_t* pos,
                                            hipStream_t stream) {
   if (B < 0) return fail(TV_ERR_INVALID_ARG, "B < 0");
-  if (N < 1 || N > TV_MAX_NODES) return fail(TV_ERR_INVALID_ARG, "N outside 1..64");
+  if (N < 1) return fail(TV_ERR_INVALID_ARG, "N < 1");
+  if (N > TV_MAX_NODES) return fail(TV_ERR_UNSUPPORTED, "N > 64");
   if (parent_sb < 0 || (parent_sb > 0 && parent_sb < N))
     return fail(TV_ERR_INVALID_ARG, "parent_sb must be 0 or >= N");
   if (B == 0) return TV_OK;
@@ -331,7 +333,8 @@ tv_status check_accept(const tv_accept_args* a) {
   if (!a) return fail(TV_ERR_INVALID_ARG, "args is null");
   if (a->dtype != TV_BF16 && a->dtype != TV_F32) return fail(TV_ERR_INVALID_ARG, "bad dtype");
   if (a->B < 0) return fail(TV_ERR_INVALID_ARG, "B < 0");
-  if (a->N < 1 || a->N > TV_MAX_NODES) return fail(TV_ERR_INVALID_ARG, "N outside 1..64");
+  if (a->N < 1) return fail(TV_ERR_INVALID_ARG, "N < 1");
+  if (a->N > TV_MAX_NODES) return fail(TV_ERR_UNSUPPORTED, "N > 64");
   if (a->V < 1) return fail(TV_ERR_INVALID_ARG, "V < 1");
   if (a->B == 0) return TV_OK;
   if (!a->logits || !a->tokens || !a->parent || !a->target || !a->accepted || !a->emitted ||
@@ -359,7 +362,8 @@ tv_status check_compact(const tv_compact_args* a) {
   if (!a) return fail(TV_ERR_INVALID_ARG, "args is null");
   if (a->dtype != TV_BF16 && a->dtype != TV_F32) return fail(TV_ERR_INVALID_ARG, "bad dtype");
   if (a->B < 0) return fail(TV_ERR_INVALID_ARG, "B < 0");
-  if (a->N < 1 || a->N > TV_MAX_NODES) return fail(TV_ERR_INVALID_ARG, "N outside 1..64");
+  if (a->N < 1) return fail(TV_ERR_INVALID_ARG, "N < 1");
+  if (a->N > TV_MAX_NODES) return fail(TV_ERR_UNSUPPORTED, "N > 64");
   if (a->Hkv < 1) return fail(TV_ERR_INVALID_ARG, "Hkv < 1");
   if (a->D != 64 && a->D != 128) return fail(TV_ERR_UNSUPPORTED, "D must be 64 or 128");
   if (a->kv_layout != TV_KV_CONTIGUOUS && a->kv_layout != TV_KV_PAGED)

@@ -238,25 +238,41 @@ extern "C" tv_status tree_meta_build_batch(const int32_t* ranks, const int64_t* 
   if (bad_tree) *bad_tree = -1;
   if (bad_path) *bad_path = -1;
   if (B < 0) return tv::fail(TV_ERR_INVALID_ARG, "B < 0");
-  if (N < 1 || N > TV_MAX_NODES) return tv::fail(TV_ERR_INVALID_ARG, "N outside 1..64");
+  if (N < 1) return tv::fail(TV_ERR_INVALID_ARG, "N < 1");
+  if (N > TV_MAX_NODES) return tv::fail(TV_ERR_UNSUPPORTED, "N > 64");
   if (B == 0) return TV_OK;
   if (!path_off || !tree_off || !prefix_len || !parent || !depth || !bitmask || !pos ||
       !num_nodes)
     return tv::fail(TV_ERR_INVALID_ARG, "null pointer");
+  // Every argument check covers the whole batch before anything is written: tree and
+  // path offsets (so no offset is dereferenced before it is known to be in order), the
+  // ranks pointer, and every prefix length.
   if (tree_off[0] != 0 || path_off[0] != 0)
     return tv::fail(TV_ERR_INVALID_ARG, "tree_off[0] and path_off[0] must be 0");
-  if (!ranks && path_off[tree_off[B]] > 0) return tv::fail(TV_ERR_INVALID_ARG, "ranks is null");
   for (int32_t b = 0; b < B; ++b) {
-    const int64_t p0 = tree_off[b], p1 = tree_off[b + 1];
-    if (p1 < p0) return tv::fail(TV_ERR_INVALID_ARG, "tree_off is not non-decreasing");
+    if (tree_off[b + 1] < tree_off[b]) {
+      if (bad_tree) *bad_tree = b;
+      return tv::fail(TV_ERR_INVALID_ARG, "tree_off is not non-decreasing");
+    }
+  }
+  const int64_t num_paths = tree_off[B];
+  for (int64_t p = 0; p < num_paths; ++p) {
+    if (path_off[p + 1] < path_off[p])
+      return tv::fail(TV_ERR_INVALID_ARG, "path_off is not non-decreasing");
+  }
+  if (!ranks && path_off[num_paths] > 0) return tv::fail(TV_ERR_INVALID_ARG, "ranks is null");
+  for (int32_t b = 0; b < B; ++b) {
     if (!prefix_ok(prefix_len[b])) {
       if (bad_tree) *bad_tree = b;
       return tv::fail(TV_ERR_INVALID_ARG, "prefix_len out of range");
     }
+  }
+  for (int32_t b = 0; b < B; ++b) {
     const size_t row = static_cast<size_t>(b) * N;
     int32_t n = 0, bad = -1;
-    const tv_status st = build_one(ranks, path_off, p0, p1, prefix_len[b], N, parent + row,
-                                   depth + row, bitmask + row, pos + row, &n, &bad);
+    const tv_status st = build_one(ranks, path_off, tree_off[b], tree_off[b + 1], prefix_len[b],
+                                   N, parent + row, depth + row, bitmask + row, pos + row, &n,
+                                   &bad);
     if (st != TV_OK) {
       if (bad_tree) *bad_tree = b;
       if (bad_path) *bad_path = bad;
