@@ -227,6 +227,24 @@ size_t tree_verify_attn_workspace_size(const tv_attn_args* a);
 tv_status tree_verify_attn(const tv_attn_args* a, hipStream_t stream);
 
 /*
+ * tree_verify_attn_static -- for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation).  Exactly
+ * tree_verify_attn (same checks, split plan, kernels and results; a->workspace and
+ * a->workspace_bytes are ignored), except that the split workspace is a fixed array of
+ * TV_STATIC_SCRATCH_BYTES that the library keeps on every device it runs on, from module
+ * load until the process ends.  It calls no allocation routine.  A plan whose workspace
+ * (tree_verify_attn_workspace_size) exceeds TV_STATIC_SCRATCH_BYTES is rejected with
+ * TV_ERR_WORKSPACE before anything is enqueued (a smaller num_splits fits; one split
+ * needs none).  All calls on one device share that device's array and it keeps the last
+ * call's contents (nothing in it needs an initial value): calls whose work overlaps on one
+ * device -- different streams, or host threads without ordering -- race on it.
+ * Errors: those of tree_verify_attn, TV_ERR_WORKSPACE as above, TV_ERR_HIP if the array's
+ * device address cannot be looked up, TV_ERR_UNSUPPORTED for a device index >= 64.
+ */
+#define TV_STATIC_SCRATCH_BYTES (64 * 1024 * 1024)
+tv_status tree_verify_attn_static(const tv_attn_args* a, hipStream_t stream);
+
+/*
  * ---- After the pass: greedy acceptance and the accepted path's KV ----
  *
  * Arguments of tree_accept_greedy.  Device memory unless stated; strides in elements.

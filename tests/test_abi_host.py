@@ -235,6 +235,22 @@ def test_workspace_size_ignores_pointers():
     assert tv.lib().tree_verify_attn_workspace_size(ctypes.byref(a)) == 8 * 8 * 40 * 129 * 4
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=0), 1), (dict(N=65), 5), (dict(D=96), 5), (dict(q=None), 1), (dict(B=-1), 1)])
+def test_static_entry_point_shares_the_argument_checks(kw, status):
+    assert tv.lib().tree_verify_attn_static(ctypes.byref(base_args(**kw)), None) == status
+
+
+def test_static_entry_point_rejects_plans_beyond_its_array():
+    # B=8, L=32768, 64 splits (57 after rounding): 8*8*57*40*129*4 bytes > 64 MiB; refused
+    # before any device call (the workspace argument is ignored: a large one does not help)
+    a = base_args(B=8, max_prefix_len=32768, num_splits=64, workspace=1 << 20,
+                  workspace_bytes=1 << 40)
+    assert tv.lib().tree_verify_attn_workspace_size(ctypes.byref(a)) > tv.STATIC_SCRATCH_BYTES
+    assert tv.lib().tree_verify_attn_static(ctypes.byref(a), None) == 6
+    assert "static scratch" in tv.lib().tv_last_error().decode()
+
+
 def test_attn_empty_batch_is_noop():
     a = base_args(B=0, q=None, k=None, v=None, out=None, parent=None, prefix_len=None)
     assert tv.lib().tree_verify_attn(ctypes.byref(a), None) == 0

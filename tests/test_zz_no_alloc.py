@@ -1,0 +1,86 @@
+"""tree_verify_attn_static (the entry point that allocates nothing) against
+tree_verify_attn, through the C ABI, on two calls in a row -- the second with a smaller
+input -- each also checked against the fp64 oracle.  Both calls split the keys, so the
+static device array carries the partials; the second call must not see anything the
+first one left in it."""
+import ctypes
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+import tree_attention_draft_amd as tv  # noqa: E402
+from tree_attention_draft_amd import workloads  # noqa: E402
+
+from gpu_cases import Case, say  # noqa: E402
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def trees(seed, B, n, cap):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return [workloads.random_tree(rng, n, cap)[0] for _ in range(B)]
+
+
+def static_call(c, out, lse, **kw):
+    """Both entry points through ctypes with the same argument struct."""
+    d = c.device()
+    a = tv.make_args(d["q"], d["k"], d["v"], d["parent"], d["prefix_len"], int(c.L.max()),
+                     out=out, lse=lse, **kw)
+    need = tv.lib().tree_verify_attn_workspace_size(ctypes.byref(a))
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    st = tv.lib().tree_verify_attn_static(ctypes.byref(a), stream)
+    assert st == 0, tv.lib().tv_last_error().decode()
+    torch.cuda.synchronize()
+    return need
+
+
+def reference_call(c, **kw):
+    d = c.device()
+    out, lse = tv.tree_verify_attn(d["q"], d["k"], d["v"], d["parent"], d["prefix_len"],
+                                   int(c.L.max()), **kw)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("kind", ["mfma", "valu_f32"])
+def test_static_entry_point_two_calls(kind):
+    if kind == "mfma":
+        big = Case("static_big", [3000, 1500, 64, 2500, 777], trees=trees(7701, 5, 33, 8),
+                   seed=7702)
+        small = Case("static_small", [900, 40], trees=trees(7703, 2, 17, 6), seed=7704)
+        kw_big, kw_small = dict(num_splits=6), dict(num_splits=3)
+    else:
+        big = Case("static_big_f32", [700, 333, 1200], trees=trees(7705, 3, 20, 6), Hq=8,
+                   Hkv=2, dtype="f32", seed=7706)
+        small = Case("static_small_f32", [90], trees=trees(7707, 1, 10, 4), Hq=4, Hkv=2,
+                     D=64, dtype="f32", seed=7708)
+        kw_big, kw_small = dict(num_splits=5), dict(num_splits=2)
+    for c, kw in ((big, kw_big), (small, kw_small)):
+        d = c.device()
+        out = torch.full_like(d["q"], float("nan"))
+        lse = torch.full((c.B, c.N, c.Hq), float("nan"), dtype=torch.float32, device="cuda")
+        need = static_call(c, out, lse, **kw)
+        assert 0 < need <= tv.STATIC_SCRATCH_BYTES
+        say(c.name, f"static call used {need} bytes of the static array")
+        ref_out, ref_lse = reference_call(c, **kw)
+        # the same kernels and plan: bit-identical to the allocating entry point
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
+        c.check(out.float().cpu().numpy().astype(np.float64),
+                lse.cpu().numpy().astype(np.float64))
+
+
+def test_static_entry_point_rejects_oversized_plans_before_enqueueing():
+    c = Case("static_reject", [4000] * 4, trees=trees(7709, 4, 33, 8), seed=7710)
+    d = c.device()
+    out = torch.full_like(d["q"], 3.0)
+    a = tv.make_args(d["q"], d["k"], d["v"], d["parent"], d["prefix_len"], 4000, out=out,
+                     num_splits=63)
+    need = tv.lib().tree_verify_attn_workspace_size(ctypes.byref(a))
+    assert need > tv.STATIC_SCRATCH_BYTES
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert tv.lib().tree_verify_attn_static(ctypes.byref(a), stream) == 6  # TV_ERR_WORKSPACE
+    assert "static scratch" in tv.lib().tv_last_error().decode()
+    torch.cuda.synchronize()
+    assert bool((out == 3.0).all())       # nothing was enqueued

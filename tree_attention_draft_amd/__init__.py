@@ -9,4 +9,5 @@ from ._binding import (  # noqa: F401
     TvCompactArgs, lib, make_accept_args, make_args, make_compact_args, tree_accept_greedy,
     tree_best_static, tree_budget_nodes, tree_budget_plan, tree_expected_tokens,
     tree_kv_compact, tree_meta_build, tree_meta_build_batch, tree_meta_from_parent,
-    tree_ridge_tokens, tree_verify_attn, tree_verify_attn_workspace_size)
+    tree_ridge_tokens, tree_verify_attn, tree_verify_attn_static,
+    tree_verify_attn_workspace_size, STATIC_SCRATCH_BYTES)

@@ -24,7 +24,8 @@ MAX_NODES = 64
 
 # Every symbol include/tree_verify.h declares.
 EXPORTS = ["tree_meta_build", "tree_meta_build_batch", "tree_meta_from_parent",
-           "tree_verify_attn_workspace_size", "tree_verify_attn", "tree_accept_greedy",
+           "tree_verify_attn_workspace_size", "tree_verify_attn", "tree_verify_attn_static",
+           "tree_accept_greedy",
            "tree_accept_greedy_workspace_size",
            "tree_kv_compact", "tree_expected_tokens", "tree_ridge_tokens",
            "tree_budget_nodes", "tree_best_static", "tree_budget_plan",
@@ -123,6 +124,8 @@ def lib():
     L.tree_verify_attn_workspace_size.argtypes = [ctypes.POINTER(TvAttnArgs)]
     L.tree_verify_attn.restype = i32
     L.tree_verify_attn.argtypes = [ctypes.POINTER(TvAttnArgs), vp]
+    L.tree_verify_attn_static.restype = i32
+    L.tree_verify_attn_static.argtypes = [ctypes.POINTER(TvAttnArgs), vp]
     L.tv_status_string.restype = ctypes.c_char_p
     L.tv_status_string.argtypes = [i32]
     L.tv_last_error.restype = ctypes.c_char_p
@@ -410,6 +413,26 @@ def tree_verify_attn(q, k, v, parent, prefix_len, max_prefix_len, *, page_table=
         a.workspace_bytes = need
     st = lib().tree_verify_attn(ctypes.byref(a), _stream(stream))
     _check(st)
+    return out, lse
+
+
+STATIC_SCRATCH_BYTES = 64 * 1024 * 1024   # TV_STATIC_SCRATCH_BYTES
+
+
+def tree_verify_attn_static(q, k, v, parent, prefix_len, max_prefix_len, *, out, lse=None,
+                            page_table=None, page_size=0, sm_scale=0.0, num_splits=0,
+                            path="auto", rope_theta=0.0, prefix_len_host=None, meta=None,
+                            stream=None):
+    """``tree_verify_attn`` without any device allocation: the caller passes ``out`` (and
+    ``lse`` if wanted); the split workspace is the library's static device array.
+    Raises TreeVerifyError (TV_ERR_WORKSPACE) when the plan needs more than
+    ``STATIC_SCRATCH_BYTES`` of workspace."""
+    _require_cuda(q, k, v, prefix_len, page_table, out, lse)
+    a = make_args(q, k, v, parent, prefix_len, max_prefix_len, page_table=page_table,
+                  page_size=page_size, sm_scale=sm_scale, out=out, lse=lse,
+                  num_splits=num_splits, path=path, rope_theta=rope_theta,
+                  prefix_len_host=prefix_len_host, meta=meta)
+    _check(lib().tree_verify_attn_static(ctypes.byref(a), _stream(stream)))
     return out, lse
 
 

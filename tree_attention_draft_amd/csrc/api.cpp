@@ -207,7 +207,7 @@ tv_status make_plan(const tv_attn_args* a, Plan* pl) {
   return TV_OK;
 }
 
-AttnParams make_params(const tv_attn_args* a, const Plan& pl) {
+AttnParams make_params(const tv_attn_args* a, const Plan& pl, void* workspace) {
   AttnParams p{};
   p.q = a->q;
   p.q_sb = a->q_sb;
@@ -259,8 +259,8 @@ AttnParams make_params(const tv_attn_args* a, const Plan& pl) {
   p.meta_bitmask = a->meta_bitmask;
   p.meta_pos = a->meta_pos;
   if (pl.splits > 1) {
-    p.ws_o = static_cast<float*>(a->workspace);
-    p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + pl.ws_o_bytes);
+    p.ws_o = static_cast<float*>(workspace);
+    p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.ws_o_bytes);
   }
   return p;
 }
@@ -284,19 +284,22 @@ extern "C" size_t tree_verify_attn_workspace_size(const tv_attn_args* a) {
   return pl.ws_bytes;
 }
 
-extern "C" tv_status tree_verify_attn(const tv_attn_args* a, hipStream_t stream) {
+namespace tv {
+
+tv_status attn_pass(const tv_attn_args* a, const WorkspaceSource& ws, hipStream_t stream) {
   tv_status st = check_args(a, true);
   if (st != TV_OK) return st;
   if (a->B == 0) return TV_OK;
   Plan pl;
   st = make_plan(a, &pl);
   if (st != TV_OK) return st;
+  void* workspace = nullptr;
   if (pl.ws_bytes > 0) {
-    if (!a->workspace || a->workspace_bytes < pl.ws_bytes)
-      return fail(TV_ERR_WORKSPACE, "workspace missing or smaller than required");
-    if (!aligned16(a->workspace)) return fail(TV_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+    st = ws.get(pl.ws_bytes, &workspace);
+    if (st != TV_OK) return st;
+    if (!aligned16(workspace)) return fail(TV_ERR_INVALID_ARG, "workspace not 16-byte aligned");
   }
-  const AttnParams p = make_params(a, pl);
+  const AttnParams p = make_params(a, pl, workspace);
   const bool bf16 = a->dtype == TV_BF16;
   hipError_t e = pl.mfma ? launch_attn_mfma(p, a->D, pl.shape, stream)
                          : launch_attn_valu(p, a->D, bf16, stream);
@@ -306,6 +309,28 @@ extern "C" tv_status tree_verify_attn(const tv_attn_args* a, hipStream_t stream)
     if (e != hipSuccess) return fail(TV_ERR_HIP, hipGetErrorString(e));
   }
   return TV_OK;
+}
+
+}  // namespace tv
+
+namespace {
+
+// The caller's workspace argument.
+struct CallerWorkspace final : tv::WorkspaceSource {
+  const tv_attn_args* a;
+  explicit CallerWorkspace(const tv_attn_args* args) : a(args) {}
+  tv_status get(size_t bytes, void** ptr) const override {
+    if (!a->workspace || a->workspace_bytes < bytes)
+      return tv::fail(TV_ERR_WORKSPACE, "workspace missing or smaller than required");
+    *ptr = a->workspace;
+    return TV_OK;
+  }
+};
+
+}  // namespace
+
+extern "C" tv_status tree_verify_attn(const tv_attn_args* a, hipStream_t stream) {
+  return tv::attn_pass(a, CallerWorkspace(a), stream);
 }
 
 extern "C" tv_status tree_meta_from_parent(const int32_t* parent, int32_t parent_sb, int32_t B,

@@ -113,4 +113,15 @@ hipError_t launch_meta_from_parent(const int32_t* parent, int32_t parent_sb, int
 
 constexpr int kValuRowsPerWg = 16;  // 4 waves x 4 rows
 
+// Where the attention pass finds its split workspace once the plan knows how many bytes it
+// needs: the caller's workspace argument, or the library's static device array.
+struct WorkspaceSource {
+  virtual tv_status get(size_t bytes, void** ptr) const = 0;
+ protected:
+  ~WorkspaceSource() = default;
+};
+
+// The whole pass (checks, plan, launches) with the workspace taken from `ws`.
+tv_status attn_pass(const tv_attn_args* a, const WorkspaceSource& ws, hipStream_t stream);
+
 }  // namespace tv
