@@ -83,14 +83,50 @@ def oracle_request(host, b, parent, L, N, page_size, rope_theta):
     return oattn.tree_attention_request(q, k, v, parent, int(L))
 
 
-def cpu_baseline(host, trees_parent, prefix_lens, N, budget_s, page_size=0, rope_theta=0.0):
-    """Time the fp64 oracle (as it stands) on whole requests until the budget is spent."""
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()
-                       if p.get("user_api") == "blas"] or [1])
+        return max([p.get("num_threads", 1) for p in threadpool_info()
+                    if p.get("user_api") == "blas"] or [1])
     except Exception:
-        threads = 1
+        return 1
+
+
+def one_thread_oracle(budget_s=2.0):
+    """The oracle on one thread (BLAS limited to 1) over the two small workloads -- the
+    worked 10-node tree at L=16 (1 head, D=64, fp32) and B=8, L=2048, 32q/8kv, D=128 with the
+    same tree -- as nodes/s, whole requests until each budget is spent."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attn as oattn
+    from oracle import meta as ometa
+    from tree_attention_draft_amd import workloads
+    out = {}
+    with threadpool_limits(limits=1):
+        for name in ("tree10_f32", "llama8b_tree10"):
+            spec = workloads.WORKLOADS[name]
+            trees, _ = workloads.trees_for(spec)
+            parent = ometa.build_from_paths(trees[0], 0)["parent"]
+            N = len(parent)
+            L = int(workloads.prefix_lengths(spec)[0])
+            host = workloads.build_batch(1000 + spec["k"], np.full(spec["B"], L, np.int32), N,
+                                         spec["Hq"], spec["Hkv"], spec["D"], spec["dtype"])
+            dec = oattn.bf16_bits_to_f64 if spec["dtype"] == "bf16" else (
+                lambda a: np.asarray(a, np.float64))
+            done, t0 = 0, time.perf_counter()
+            while time.perf_counter() - t0 < budget_s:
+                b = done % spec["B"]
+                oattn.tree_attention_request(dec(host["q"][b]), dec(host["k"][b, :L + N]),
+                                             dec(host["v"][b, :L + N]), parent, L)
+                done += 1
+            out[name] = done * N / (time.perf_counter() - t0)
+    return out
+
+
+def cpu_baseline(host, trees_parent, prefix_lens, N, budget_s, page_size=0, rope_theta=0.0):
+    """Time the fp64 oracle (as it stands) on whole requests until the budget is spent."""
+    threads = blas_threads()
     B = len(prefix_lens)
     done = 0
     t0 = time.perf_counter()
@@ -100,10 +136,12 @@ def cpu_baseline(host, trees_parent, prefix_lens, N, budget_s, page_size=0, rope
         oracle_request(host, b, trees_parent[b], prefix_lens[b], N, page_size, rope_theta)
         done += 1
     el = time.perf_counter() - t0
-    return {"value": done * N / el, "unit": "nodes/s", "cores": int(threads),
+    return {"value": done * N / el, "unit": "nodes/s",
+            "cores": len(os.sched_getaffinity(0)), "blas_threads": int(threads),
             "kind": "oracle",
             "sample": f"{done} whole requests ({done / B:.1f} passes over the {B}-request "
-                      f"batch; all nodes and heads), fp64 numpy oracle, {el:.1f} s"}
+                      f"batch; all nodes and heads), fp64 numpy oracle, {el:.1f} s",
+            "one_thread_nodes_per_s": one_thread_oracle()}
 
 
 def bench_after_pass(args):
@@ -123,7 +161,10 @@ def bench_after_pass(args):
     B, N, Hkv, D, Lp = spec["B"], spec["N"], spec["Hkv"], spec["D"], spec["L"]
     V = 128256
     trees, _ = workloads.trees_for(spec)
-    parents = [ometa.build_from_paths(t, 0)["parent"] for t in trees]
+    # the product's inputs come from the library's batched builder; the oracle only checks
+    built = tv.tree_meta_build_batch(tv.PackedTrees(trees), np.zeros(B, np.int32), N)
+    parents = built["parent"].tolist()
+    assert parents == [ometa.build_from_paths(t, 0)["parent"] for t in trees]
     par = torch.tensor(np.array(parents, np.int32), device=dev)
     g = torch.Generator(device=dev)
     g.manual_seed(1234)

@@ -269,7 +269,7 @@ tv_status tree_verify_attn_static(const tv_attn_args* a, hipStream_t stream);
  *                         initialisation.
  */
 typedef struct {
-  tv_dtype dtype;
+  int32_t dtype;           /* tv_dtype, held as a plain int so any value can be checked */
   int32_t B, N, V;
   const void* logits;
   int64_t lg_sb, lg_sn;
@@ -326,9 +326,9 @@ tv_status tree_accept_greedy(const tv_accept_args* a, hipStream_t stream);
  *                         unchanged.
  */
 typedef struct {
-  tv_dtype dtype;
+  int32_t dtype;           /* tv_dtype, held as a plain int so any value can be checked */
   int32_t B, N, Hkv, D;
-  tv_kv_layout kv_layout;
+  int32_t kv_layout;       /* tv_kv_layout */
   void* k;
   void* v;
   int64_t kv_sb, kv_st, kv_sh;
