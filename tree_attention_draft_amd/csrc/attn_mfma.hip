@@ -366,6 +366,7 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
   constexpr int TT = TN + RR;  // tiles of state per wave: full tiles, then the shared one
   __shared__ __attribute__((aligned(1024))) char smem[NST * C::STAGEB];
   __shared__ uint64_t mask_s[TV_MAX_NODES];
+  __shared__ int32_t par_s[TV_MAX_NODES];
   __shared__ int32_t pt_s[kMaxPageSlice];
   // the shared remainder tile's query operands (B-operand layout, [k-step][lane]): read
   // from LDS on the key tiles a wave computes it, so they take no registers in the loop
@@ -438,10 +439,15 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
     }
   }
 
+  // The parent array is staged in LDS with one coalesced load, so that each node's walk up
+  // to the root chases its parent links through LDS rather than through global memory (a
+  // round trip per level, all before the key ring may start).
+  if (tid < p.N) par_s[tid] = p.parent[(int64_t)b * p.parent_sb + tid];
+  __syncthreads();
   if (tid < p.N) {
     bool ok;
     int dd;
-    const uint64_t m = ancestor_bits(p.parent + (int64_t)b * p.parent_sb, tid, p.N, ok, dd);
+    const uint64_t m = ancestor_bits(par_s, tid, p.N, ok, dd);
     mask_s[tid] = m;
     // one workgroup per request (split 0, first row chunk of kv head 0) exports the tree
     if (split == 0 && blockIdx.y == 0) export_node_meta(p, b, tid, m, ok, dd);

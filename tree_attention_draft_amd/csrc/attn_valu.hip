@@ -39,6 +39,7 @@ __global__ void __launch_bounds__(256) tv_attn_valu_kernel(AttnParams p) {
   __shared__ float Qs[ROWS][D];
   __shared__ float Ps[4][KT];
   __shared__ uint64_t mask_s[TV_MAX_NODES];
+  __shared__ int32_t par_s[TV_MAX_NODES];
 
   const int split = blockIdx.x;
   const int hkv = blockIdx.y % p.Hkv;
@@ -57,10 +58,13 @@ __global__ void __launch_bounds__(256) tv_attn_valu_kernel(AttnParams p) {
   const T* __restrict__ kp = static_cast<const T*>(p.k);
   const T* __restrict__ vp = static_cast<const T*>(p.v);
 
+  // parent links staged in LDS: the walks below then take no global round trip per level
+  if (tid < p.N) par_s[tid] = p.parent[(int64_t)b * p.parent_sb + tid];
+  __syncthreads();
   if (tid < p.N) {
     bool ok;
     int dd;
-    const uint64_t m = ancestor_bits(p.parent + (int64_t)b * p.parent_sb, tid, p.N, ok, dd);
+    const uint64_t m = ancestor_bits(par_s, tid, p.N, ok, dd);
     mask_s[tid] = m;
     // one workgroup per request (split 0, first row chunk of kv head 0) exports the tree
     if (blockIdx.x == 0 && blockIdx.y == 0) export_node_meta(p, b, tid, m, ok, dd);
