@@ -164,10 +164,11 @@ tv_status make_plan(const tv_attn_args* a, Plan* pl) {
     // chunks of two thirds of that average, so that its long requests spread over several
     // workgroups taken first (on MI355X, B=64, L ~ U[512, 8192]: 264 us against 281 us
     // with one split and 323 us with chunks of the average)
-    // When that leaves a workgroup under 16 key tiles (small batches), chunks are sized
-    // for one workgroup per compute unit instead: each workgroup pays a prologue and a
-    // partial of R*(D+1)*4 bytes, which short chunks cannot hide (paged L=32768, B=1:
-    // 80 us at 32 splits against 91 us at 57; L=2048, B=8: 26.7 us at 4 against 29.7 at 7).
+    // When that leaves a workgroup under 8 chunk units of 64 keys (small batches), chunks
+    // are sized for one workgroup per compute unit instead: each workgroup pays a prologue
+    // and a partial of R*(D+1)*4 bytes, which short chunks cannot hide (MI355X, L=2048,
+    // B=8: 24.5 us at 4 splits against 25.7 at 6 and 25.9 at 8; paged L=32768, B=1, nine
+    // units a workgroup at two per unit: 59.4 us at 61 splits against 65.6 at 31).
     // Slots: two workgroups per compute unit, one for the eight-wave shapes (their register
     // use allows two waves per SIMD, i.e. eight waves per unit; B=16,
     // N=64, 64q/8kv: 152 us with one split against 183 us with the two that two slots
@@ -175,7 +176,7 @@ tv_status make_plan(const tv_attn_args* a, Plan* pl) {
     const int64_t cus = device_cu_count();
     const int64_t per_cu = pl->mfma && pl->shape.nw >= 8 ? 1 : 2;
     int64_t avg = (pair_tiles + per_cu * cus - 1) / (per_cu * cus);
-    if (avg < 16) avg = (pair_tiles + cus - 1) / cus;
+    if (avg < 8) avg = (pair_tiles + cus - 1) / cus;
     const int64_t chunk_tiles = std::max<int64_t>(1, ragged ? (2 * avg + 2) / 3 : avg);
     S = (tiles + chunk_tiles - 1) / chunk_tiles;
   }

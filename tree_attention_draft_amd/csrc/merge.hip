@@ -7,7 +7,13 @@
 // i.e. the softmax over the union of the chunks.  Requests with fewer splits than the grid
 // contribute only their own ceil((L + N) / chunk) partials; a request whose keys fit one
 // chunk was written directly by the attention kernel and is skipped here.
-// One thread per (request, kv head, packed row, 4 features).
+// One thread per (request, kv head, packed row, 4 features).  The sum runs online over
+// groups of partials (16 while that many remain, then 4): all loads of a group are issued
+// before any of them is used (a thread walking many splits one at a time would wait a
+// memory round trip per split), and the running sum is moved to each group's max as it
+// goes.
+#include <type_traits>
+
 #include "kernels_common.h"
 
 namespace tv {
@@ -29,21 +35,40 @@ __global__ void __launch_bounds__(256) tv_merge_kernel(AttnParams p) {
   if (ns <= 1) return;  // one split: the attention kernel wrote the final output
 
   const int64_t base = ((int64_t)b * p.Hkv + hkv) * p.num_splits;
-  float mx = -INFINITY;
-  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, p.ws_lse[(base + s) * p.R + row]);
-  float wsum = 0.f;
+  float mx = -INFINITY;  // max of the log-sum-exps seen so far
+  float wsum = 0.f;      // sum of 2^(lse_s - mx) so far
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (mx != -INFINITY) {
-    for (int s = 0; s < ns; ++s) {
-      const int64_t prow = (base + s) * p.R + row;
-      const float ls = p.ws_lse[prow];
-      if (ls == -INFINITY) continue;  // no allowed key in this chunk: weight 0
-      const float wgt = exp2f(ls - mx);
-      wsum += wgt;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(p.ws_o + prow * D + 4 * q4);
-      acc += v * wgt;
+  auto group = [&](int s0, auto size_c) {
+    constexpr int G = decltype(size_c)::value;
+    float ls[G];
+    f32x4 v[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      // past the last split: re-read the last partial (in bounds) and give it no weight
+      const int64_t prow = (base + min(s0 + u, ns - 1)) * p.R + row;
+      const float l = p.ws_lse[prow];
+      ls[u] = s0 + u < ns ? l : -INFINITY;
+      v[u] = *reinterpret_cast<const f32x4*>(p.ws_o + prow * D + 4 * q4);
     }
-  }
+    float mg = mx;
+#pragma unroll
+    for (int u = 0; u < G; ++u) mg = fmaxf(mg, ls[u]);
+    if (mg == -INFINITY) return;  // no allowed key in any chunk so far
+    const float sc = exp2f(mx - mg);  // 0 while mx is still -inf
+    wsum *= sc;
+    acc *= sc;
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      // a chunk with no allowed key (lse -inf) weighs 0
+      const float wgt = ls[u] == -INFINITY ? 0.f : exp2f(ls[u] - mg);
+      wsum += wgt;
+      acc += v[u] * wgt;
+    }
+    mx = mg;
+  };
+  int s0 = 0;
+  for (; s0 + 16 <= ns; s0 += 16) group(s0, std::integral_constant<int, 16>{});
+  for (; s0 < ns; s0 += 4) group(s0, std::integral_constant<int, 4>{});
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   const int node = row / p.g, head = hkv * p.g + row % p.g;
   T* out = static_cast<T*>(p.out) + (int64_t)b * p.o_sb + (int64_t)node * p.o_sn +
