@@ -36,7 +36,7 @@ extern "C" {
 #endif
 
 #define TV_MAX_NODES 64
-#define TV_ABI_VERSION 4
+#define TV_ABI_VERSION 5
 
 typedef enum {
   TV_OK = 0,
@@ -304,7 +304,62 @@ size_t tree_accept_greedy_workspace_size(const tv_accept_args* a);
  */
 tv_status tree_accept_greedy(const tv_accept_args* a, hipStream_t stream);
 
+
+
 /*
+ * Arguments of tree_accept_stochastic.  Device memory unless stated; strides in elements.
+ *   B, N, V               requests (>= 0), tree nodes (1..TV_MAX_NODES), vocabulary (>= 1).
+ *   p [B, N, V]           float32: the target's next-token distribution after every node
+ *                         (need not be normalised; every row the walk reads must be finite,
+ *                         non-negative, with positive mass); p_sb, p_sn strides (>= 0).
+ *   q [B, N, V]           float32: the drafter's distribution at every node, the one the
+ *                         node's children were drawn from, i.i.d. (rows of leaves are not
+ *                         read; same rules as p); q_sb, q_sn.
+ *   tokens [B, N]         draft tokens in [0, V) (node 0's is not read); tokens_sb (0 = one
+ *                         row for all requests).
+ *   parent [B, N]         the tree, parent-before-child; parent_sb (0 = one tree for all).
+ *   uniform [B, N]        float64 in [0, 1): uniform[c] drives child c's acceptance test,
+ *                         uniform[0] the final draw (the root is never tested); uniform_sb
+ *                         (0 = one row for all requests).
+ * Outputs (caller-owned device memory, [B, N] int32 unless stated): accepted, emitted and
+ *   num_accepted [B] exactly as tree_accept_greedy defines them.
+ */
+typedef struct {
+  int32_t B, N, V;
+  const float* p;
+  int64_t p_sb, p_sn;
+  const float* q;
+  int64_t q_sb, q_sn;
+  const int32_t* tokens;
+  int32_t tokens_sb;
+  const int32_t* parent;
+  int32_t parent_sb;
+  const double* uniform;
+  int32_t uniform_sb;
+  int32_t* accepted;
+  int32_t* emitted;
+  int32_t* num_accepted;
+} tv_sample_args;
+
+/*
+ * tree_accept_stochastic -- lossless verification of the tree at temperature > 0
+ * ("Implement a batched speculative sampling verifier", "A strong answer": the accept test
+ * u * q < p, the residual max(0, p - q), the inverse-CDF draw and the p = q corner; "What
+ * interviewers probe next": the tree is walked with the same rule, each sibling after a
+ * rejection judged against the residual; "Tree Verification", "Accepting on a Tree").
+ * Per request, from the root: r starts as the node's p; each child c in node order, token
+ * x, is accepted when uniform[c] * q(x) * sum(r) < r(x); after a rejection r becomes
+ * max(0, r / sum(r) - q) (unchanged if that has no mass).  The first accepted child
+ * becomes the current node and its token is emitted; if none is (or at a leaf) one token
+ * is drawn from r by inverse CDF with uniform[0] -- the first index whose running sum
+ * exceeds uniform[0] * sum(r), the last index of positive weight if none does -- and the
+ * walk stops.  All of this arithmetic is float64.  A child whose token lies outside
+ * [0, V) is never accepted and leaves r unchanged; a final draw from a row with no mass
+ * emits -1.  Enqueues one kernel on `stream` (one workgroup per request; one pass over a
+ * node's p and q rows per test).  Needs no workspace.  Errors: TV_ERR_INVALID_ARG (null pointers, sizes, strides), TV_ERR_UNSUPPORTED
+ * (N > 64), TV_ERR_HIP.  B == 0 is a no-op.
+ */
+tv_status tree_accept_stochastic(const tv_sample_args* a, hipStream_t stream);/*
  * Arguments of tree_kv_compact.  The KV cache as in tv_attn_args (contiguous or paged;
  * k and v are written in place) and, per request:
  *   prefix_len [B]        L before the verified tree (tree node i sits at logical L + i);
@@ -452,8 +507,9 @@ int32_t tv_abi_version(void);
 /* sizeof(tv_attn_args) as compiled into the library, for bindings to check their mirror. */
 size_t tv_attn_args_sizeof(void);
 
-/* sizeof(tv_accept_args) and sizeof(tv_compact_args), likewise. */
+/* sizeof(tv_accept_args), sizeof(tv_sample_args) and sizeof(tv_compact_args), likewise. */
 size_t tv_accept_args_sizeof(void);
+size_t tv_sample_args_sizeof(void);
 size_t tv_compact_args_sizeof(void);
 
 #ifdef __cplusplus

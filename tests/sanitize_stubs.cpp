@@ -16,6 +16,7 @@ hipError_t launch_meta_from_parent(const int32_t*, int32_t, int32_t, int32_t, co
 }
 hipError_t launch_argmax(const AcceptParams&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_compact(const CompactParams&, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_stochastic_walk(const SampleParams&, hipStream_t) { return hipErrorNoDevice; }
 }  // namespace tv
 
 // The no-allocation entry point without its device array: the same checks, plan and size

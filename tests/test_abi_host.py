@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_struct_and_version():
     L = tv.lib()
-    assert L.tv_abi_version() == 4
+    assert L.tv_abi_version() == 5
     assert L.tv_attn_args_sizeof() == ctypes.sizeof(TvAttnArgs)
     for code in range(8):
         assert L.tv_status_string(code).decode().startswith("TV_")
@@ -376,6 +376,39 @@ def test_accept_empty_batch_is_noop():
     assert tv.lib().tree_accept_greedy(ctypes.byref(a), None) == 0
 
 
+def base_sample_args(**kw):
+    a = tv.TvSampleArgs()
+    a.B, a.N, a.V = 2, 10, 1000
+    fake = 1 << 20  # never dereferenced: every case below fails validation first
+    a.p = a.q = a.tokens = a.parent = a.uniform = fake
+    a.accepted = a.emitted = a.num_accepted = fake
+    a.p_sb = a.q_sb = 10 * 1000
+    a.p_sn = a.q_sn = 1000
+    a.tokens_sb = a.parent_sb = a.uniform_sb = 10
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=0), 1), (dict(V=0), 1), (dict(B=-1), 1), (dict(N=65), 5), (dict(B=70000), 5),
+    (dict(p=None), 1), (dict(q=None), 1), (dict(tokens=None), 1), (dict(parent=None), 1),
+    (dict(uniform=None), 1), (dict(accepted=None), 1), (dict(emitted=None), 1),
+    (dict(num_accepted=None), 1), (dict(p_sn=999), 1), (dict(q_sb=5000), 1),
+    (dict(p_sb=-1), 1), (dict(tokens_sb=3), 1), (dict(parent_sb=9), 1),
+    (dict(uniform_sb=9), 1), (dict(p=(1 << 20) + 2), 1), (dict(uniform=(1 << 20) + 4), 1),
+])
+def test_stochastic_accept_argument_checks(kw, status):
+    L = tv.lib()
+    assert L.tree_accept_stochastic(ctypes.byref(base_sample_args(**kw)), None) == status
+    assert L.tv_last_error().decode() != ""
+
+
+def test_stochastic_accept_empty_batch_is_noop():
+    a = base_sample_args(B=0, p=None, q=None, tokens=None, parent=None, uniform=None)
+    assert tv.lib().tree_accept_stochastic(ctypes.byref(a), None) == 0
+
+
 def base_compact_args(**kw):
     a = tv.TvCompactArgs()
     a.dtype, a.B, a.N, a.Hkv, a.D = 0, 2, 10, 8, 128
@@ -413,4 +446,5 @@ def test_compact_empty_batch_is_noop():
 def test_after_pass_struct_sizes():
     L = tv.lib()
     assert L.tv_accept_args_sizeof() == ctypes.sizeof(tv.TvAcceptArgs)
+    assert L.tv_sample_args_sizeof() == ctypes.sizeof(tv.TvSampleArgs)
     assert L.tv_compact_args_sizeof() == ctypes.sizeof(tv.TvCompactArgs)

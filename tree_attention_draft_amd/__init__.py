@@ -6,7 +6,8 @@ Python binding plus the seeded workload generators used by the tests and the ben
 """
 from ._binding import (  # noqa: F401
     EXPORTS, LIB_PATH, MAX_NODES, PackedTrees, TreeVerifyError, TvAcceptArgs, TvAttnArgs,
-    TvCompactArgs, lib, make_accept_args, make_args, make_compact_args, tree_accept_greedy,
+    TvCompactArgs, TvSampleArgs, lib, make_accept_args, make_args, make_compact_args,
+    make_sample_args, tree_accept_greedy, tree_accept_stochastic,
     tree_best_static, tree_budget_nodes, tree_budget_plan, tree_expected_tokens,
     tree_kv_compact, tree_meta_build, tree_meta_build_batch, tree_meta_from_parent,
     tree_ridge_tokens, tree_verify_attn, tree_verify_attn_static,

@@ -26,11 +26,12 @@ MAX_NODES = 64
 EXPORTS = ["tree_meta_build", "tree_meta_build_batch", "tree_meta_from_parent",
            "tree_verify_attn_workspace_size", "tree_verify_attn", "tree_verify_attn_static",
            "tree_accept_greedy",
-           "tree_accept_greedy_workspace_size",
+           "tree_accept_greedy_workspace_size", "tree_accept_stochastic",
            "tree_kv_compact", "tree_expected_tokens", "tree_ridge_tokens",
            "tree_budget_nodes", "tree_best_static", "tree_budget_plan",
            "tv_status_string", "tv_last_error", "tv_abi_version", "tv_pinned_device_address",
-           "tv_attn_args_sizeof", "tv_accept_args_sizeof", "tv_compact_args_sizeof"]
+           "tv_attn_args_sizeof", "tv_accept_args_sizeof", "tv_sample_args_sizeof",
+           "tv_compact_args_sizeof"]
 
 
 class TreeVerifyError(RuntimeError):
@@ -80,6 +81,20 @@ class TvAcceptArgs(ctypes.Structure):
         ("target", ctypes.c_void_p), ("accepted", ctypes.c_void_p),
         ("emitted", ctypes.c_void_p), ("num_accepted", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class TvSampleArgs(ctypes.Structure):
+    """Mirror of ``tv_sample_args``."""
+    _fields_ = [
+        ("B", ctypes.c_int32), ("N", ctypes.c_int32), ("V", ctypes.c_int32),
+        ("p", ctypes.c_void_p), ("p_sb", ctypes.c_int64), ("p_sn", ctypes.c_int64),
+        ("q", ctypes.c_void_p), ("q_sb", ctypes.c_int64), ("q_sn", ctypes.c_int64),
+        ("tokens", ctypes.c_void_p), ("tokens_sb", ctypes.c_int32),
+        ("parent", ctypes.c_void_p), ("parent_sb", ctypes.c_int32),
+        ("uniform", ctypes.c_void_p), ("uniform_sb", ctypes.c_int32),
+        ("accepted", ctypes.c_void_p), ("emitted", ctypes.c_void_p),
+        ("num_accepted", ctypes.c_void_p),
     ]
 
 
@@ -138,6 +153,9 @@ def lib():
     L.tree_accept_greedy_workspace_size.argtypes = [ctypes.POINTER(TvAcceptArgs)]
     L.tree_accept_greedy.restype = i32
     L.tree_accept_greedy.argtypes = [ctypes.POINTER(TvAcceptArgs), vp]
+    L.tree_accept_stochastic.restype = i32
+    L.tree_accept_stochastic.argtypes = [ctypes.POINTER(TvSampleArgs), vp]
+    L.tv_sample_args_sizeof.restype = ctypes.c_size_t
     L.tree_kv_compact.restype = i32
     L.tree_kv_compact.argtypes = [ctypes.POINTER(TvCompactArgs), vp]
     L.tv_accept_args_sizeof.restype = ctypes.c_size_t
@@ -446,11 +464,12 @@ def default_scale(D):
 
 
 # ------------------------------------------------------------ after the pass --------
-def _rows(t, name, B, N):
-    """Request stride of an int32 [B, N] (or shared [N]) tensor."""
+def _rows(t, name, B, N, dtype=None):
+    """Request stride of an int32 (or ``dtype``) [B, N] (or shared [N]) tensor."""
     torch = _torch()
-    if t.dtype != torch.int32:
-        raise ValueError(f"{name} must be int32")
+    dtype = torch.int32 if dtype is None else dtype
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}")
     if t.dim() == 1:
         if t.shape[0] != N:
             raise ValueError(f"{name} must have N entries")
@@ -513,6 +532,54 @@ def tree_accept_greedy(logits, tokens, parent, target=None, accepted=None, emitt
     a.workspace_bytes = workspace.numel() * workspace.element_size()
     _check(lib().tree_accept_greedy(ctypes.byref(a), _stream(stream)))
     return target, accepted, emitted, num_accepted
+
+
+def make_sample_args(p, q, tokens, parent, uniform, accepted, emitted, num_accepted):
+    torch = _torch()
+    if p.dim() != 3 or q.shape != p.shape:
+        raise ValueError("p and q must be [B, N, V] of the same shape")
+    for t, n in ((p, "p"), (q, "q")):
+        if t.dtype != torch.float32 or t.stride(2) != 1:
+            raise ValueError(f"{n} must be float32, contiguous along the vocabulary")
+    B, N, V = p.shape
+    a = TvSampleArgs()
+    a.B, a.N, a.V = B, N, V
+    a.p, a.p_sb, a.p_sn = p.data_ptr(), p.stride(0), p.stride(1)
+    a.q, a.q_sb, a.q_sn = q.data_ptr(), q.stride(0), q.stride(1)
+    a.tokens_sb = _rows(tokens, "tokens", B, N)
+    a.tokens = tokens.data_ptr()
+    a.parent_sb = _rows(parent, "parent", B, N)
+    a.parent = parent.data_ptr()
+    a.uniform_sb = _rows(uniform, "uniform", B, N, torch.float64)
+    a.uniform = uniform.data_ptr()
+    for t, n in ((accepted, "accepted"), (emitted, "emitted")):
+        if t.dtype != torch.int32 or tuple(t.shape) != (B, N) or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous int32 [B, N] tensor")
+    if num_accepted.dtype != torch.int32 or tuple(num_accepted.shape) != (B,):
+        raise ValueError("num_accepted must be int32 [B]")
+    a.accepted, a.emitted = accepted.data_ptr(), emitted.data_ptr()
+    a.num_accepted = num_accepted.data_ptr()
+    return a
+
+
+def tree_accept_stochastic(p, q, tokens, parent, uniform, accepted=None, emitted=None,
+                           num_accepted=None, stream=None):
+    """Stochastic verification: target ``p`` and drafter ``q`` distributions [B, N, V]
+    (float32), draft ``tokens``, ``parent`` int32 and ``uniform`` float64 in [0, 1), each
+    [B, N] (or [N] shared).  Returns ``(accepted, emitted, num_accepted)`` as
+    tree_accept_greedy does."""
+    torch = _torch()
+    _require_cuda(p, q, tokens, parent, uniform, accepted, emitted, num_accepted)
+    B, N, _ = p.shape
+    dev = p.device
+    def mk(t, shape):
+        return torch.empty(shape, dtype=torch.int32, device=dev) if t is None else t
+    with _on(stream):
+        accepted, emitted = mk(accepted, (B, N)), mk(emitted, (B, N))
+        num_accepted = mk(num_accepted, (B,))
+    a = make_sample_args(p, q, tokens, parent, uniform, accepted, emitted, num_accepted)
+    _check(lib().tree_accept_stochastic(ctypes.byref(a), _stream(stream)))
+    return accepted, emitted, num_accepted
 
 
 def make_compact_args(k, v, prefix_len, max_prefix_len, parent, accepted, num_accepted,

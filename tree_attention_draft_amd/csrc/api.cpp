@@ -384,6 +384,34 @@ tv_status check_accept(const tv_accept_args* a) {
   return TV_OK;
 }
 
+tv_status check_sample(const tv_sample_args* a) {
+  if (!a) return fail(TV_ERR_INVALID_ARG, "args is null");
+  if (a->B < 0) return fail(TV_ERR_INVALID_ARG, "B < 0");
+  if (a->N < 1) return fail(TV_ERR_INVALID_ARG, "N < 1");
+  if (a->N > TV_MAX_NODES) return fail(TV_ERR_UNSUPPORTED, "N > 64");
+  if (a->V < 1) return fail(TV_ERR_INVALID_ARG, "V < 1");
+  if (a->V > (1 << 30)) return fail(TV_ERR_INVALID_ARG, "V > 2^30");
+  if (a->B == 0) return TV_OK;
+  if (!a->p || !a->q || !a->tokens || !a->parent || !a->uniform || !a->accepted ||
+      !a->emitted || !a->num_accepted)
+    return fail(TV_ERR_INVALID_ARG, "null pointer argument");
+  const int64_t rows[][2] = {{a->p_sb, a->p_sn}, {a->q_sb, a->q_sn}};
+  for (const auto& r : rows)
+    if (r[1] < a->V || r[0] < 0 || (a->B > 1 && r[0] < (int64_t)a->N * r[1]))
+      return fail(TV_ERR_INVALID_ARG, "p and q strides must cover [B, N, V] without overlap");
+  if (a->tokens_sb != 0 && a->tokens_sb < a->N)
+    return fail(TV_ERR_INVALID_ARG, "tokens_sb must be 0 or >= N");
+  if (a->parent_sb != 0 && a->parent_sb < a->N)
+    return fail(TV_ERR_INVALID_ARG, "parent_sb must be 0 or >= N");
+  if (a->uniform_sb != 0 && a->uniform_sb < a->N)
+    return fail(TV_ERR_INVALID_ARG, "uniform_sb must be 0 or >= N");
+  if ((reinterpret_cast<uintptr_t>(a->p) | reinterpret_cast<uintptr_t>(a->q)) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(a->uniform) % 8 != 0)
+    return fail(TV_ERR_INVALID_ARG, "p, q or uniform not aligned to its element size");
+  if (a->B > 65535) return fail(TV_ERR_UNSUPPORTED, "B > 65535");
+  return TV_OK;
+}
+
 tv_status check_compact(const tv_compact_args* a) {
   if (!a) return fail(TV_ERR_INVALID_ARG, "args is null");
   if (a->dtype != TV_BF16 && a->dtype != TV_F32) return fail(TV_ERR_INVALID_ARG, "bad dtype");
@@ -452,6 +480,35 @@ extern "C" tv_status tree_accept_greedy(const tv_accept_args* a, hipStream_t str
   return TV_OK;
 }
 
+extern "C" tv_status tree_accept_stochastic(const tv_sample_args* a, hipStream_t stream) {
+  using namespace tv;
+  tv_status st = check_sample(a);
+  if (st != TV_OK) return st;
+  if (a->B == 0) return TV_OK;
+  SampleParams p;
+  p.B = a->B;
+  p.N = a->N;
+  p.V = a->V;
+  p.p = a->p;
+  p.p_sb = a->p_sb;
+  p.p_sn = a->p_sn;
+  p.q = a->q;
+  p.q_sb = a->q_sb;
+  p.q_sn = a->q_sn;
+  p.tokens = a->tokens;
+  p.tokens_sb = a->tokens_sb;
+  p.parent = a->parent;
+  p.parent_sb = a->parent_sb;
+  p.uniform = a->uniform;
+  p.uniform_sb = a->uniform_sb;
+  p.accepted = a->accepted;
+  p.emitted = a->emitted;
+  p.num_accepted = a->num_accepted;
+  const hipError_t e = launch_stochastic_walk(p, stream);
+  if (e != hipSuccess) return fail(TV_ERR_HIP, hipGetErrorString(e));
+  return TV_OK;
+}
+
 extern "C" tv_status tree_kv_compact(const tv_compact_args* a, hipStream_t stream) {
   using namespace tv;
   tv_status st = check_compact(a);
@@ -494,6 +551,7 @@ extern "C" size_t tree_accept_greedy_workspace_size(const tv_accept_args* a) {
 }
 
 extern "C" size_t tv_accept_args_sizeof(void) { return sizeof(tv_accept_args); }
+extern "C" size_t tv_sample_args_sizeof(void) { return sizeof(tv_sample_args); }
 extern "C" size_t tv_compact_args_sizeof(void) { return sizeof(tv_compact_args); }
 
 extern "C" const char* tv_status_string(tv_status s) {

@@ -80,6 +80,24 @@ struct AcceptParams {
   void* workspace;  // B*N*ceil(V/kArgSlice) uint64 slice keys
 };
 
+// Device-side arguments of the stochastic walk kernel.
+struct SampleParams {
+  int B, N, V;
+  const float* p;
+  int64_t p_sb, p_sn;
+  const float* q;
+  int64_t q_sb, q_sn;
+  const int32_t* tokens;
+  int tokens_sb;
+  const int32_t* parent;
+  int parent_sb;
+  const double* uniform;
+  int uniform_sb;
+  int32_t* accepted;
+  int32_t* emitted;
+  int32_t* num_accepted;
+};
+
 // Device-side arguments of the KV compaction kernel.
 struct CompactParams {
   bool bf16, paged;
@@ -103,6 +121,7 @@ struct CompactParams {
 
 hipError_t launch_argmax(const AcceptParams& p, hipStream_t s);
 hipError_t launch_compact(const CompactParams& p, hipStream_t s);
+hipError_t launch_stochastic_walk(const SampleParams& p, hipStream_t s);
 
 hipError_t launch_attn_mfma(const AttnParams& p, int D, MfmaShape shape, hipStream_t s);
 hipError_t launch_attn_valu(const AttnParams& p, int D, bool bf16, hipStream_t s);

@@ -76,6 +76,21 @@ def random_root_path(rng, parent):
     return up[::-1]
 
 
+def random_parent(rng, n_nodes):
+    """A random parent-before-child array: node i's parent drawn uniformly from 0..i-1."""
+    return [-1] + [int(rng.integers(0, i)) for i in range(1, n_nodes)]
+
+
+def random_distributions(rng, shape, temperature=1.0):
+    """float32 next-token distributions over the last axis: a softmax of standard-normal
+    logits scaled by 1 / temperature (inputs for the acceptance walks, which take
+    probabilities, not logits)."""
+    z = rng.standard_normal(size=shape) / temperature
+    z -= z.max(axis=-1, keepdims=True)
+    e = np.exp(z)
+    return (e / e.sum(axis=-1, keepdims=True)).astype(np.float32)
+
+
 def normal_f32(rng, shape):
     return rng.standard_normal(size=shape, dtype=np.float32)
 
