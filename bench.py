@@ -146,8 +146,9 @@ def cpu_baseline(host, trees_parent, prefix_lens, N, budget_s, page_size=0, rope
 
 def bench_after_pass(args):
     """Time the after-pass entry points at the B=64, N=33 batch: greedy acceptance over
-    Llama-3-sized logits (V=128256, bf16; the argmax reads 541 MB), and the accepted-path
-    KV compaction on the L=4096, 8 kv-head, D=128 cache.  One JSON line per stage."""
+    Llama-3-sized logits (V=128256, bf16; the argmax reads 541 MB), stochastic acceptance
+    over float32 distributions of the same size, and the accepted-path KV compaction on
+    the L=4096, 8 kv-head, D=128 cache.  One JSON line per stage."""
     import numpy as np
     import torch
 
@@ -221,6 +222,45 @@ def bench_after_pass(args):
                      "traffic": None, "kernel": "tv_argmax_kernel + tv_walk_kernel",
                      "kernel_p10_p50_p90_us": pct, "algorithmic_bytes_per_launch": abytes},
         "parity": {"requests": [0, B - 1], "ok": bool(ok)}}), flush=True)
+
+    # ---- stochastic acceptance at temperature 1: target p = softmax of the same logits,
+    # drafter q = softmax of independent logits, every child drawn from its parent's q ----
+    p = torch.softmax(logits.float(), -1)
+    q = torch.softmax(torch.randn((B, N, V), generator=g, device=dev) * 3, -1)
+    pidx = torch.tensor([[max(x, 0) for x in row] for row in parents], device=dev)
+    qpar = q[torch.arange(B, device=dev)[:, None], pidx].reshape(B * N, V)
+    stok = torch.multinomial(qpar, 1, generator=g).reshape(B, N).to(torch.int32)
+    del qpar
+    unif = torch.rand((B, N), generator=g, device=dev, dtype=torch.float64)
+    t_s, pct_s = timed(lambda: tv.tree_accept_stochastic(p, q, stok, par, unif, acc, em, na),
+                       args.steps, args.warmup)
+    ok_s = True
+    for b in (0, B - 1):
+        a_ref, e_ref = oacc.accept_stochastic(parents[b], stok[b].cpu().numpy(),
+                                              p[b].cpu().numpy(), q[b].cpu().numpy(),
+                                              unif[b].cpu().numpy())
+        ok_s &= acc[b, :len(a_ref)].tolist() == a_ref and em[b, :len(e_ref)].tolist() == e_ref
+    # algorithmic bytes: every visited node's p row, and its q row where children were tested
+    has_child = [set(row[1:]) for row in parents]
+    sbytes = 4 * B * N * 3 + 8 * B * N + 4 * B
+    for b in range(B):
+        for node in acc[b, :int(na[b])].tolist():
+            sbytes += 4 * V * (2 if node in has_child[b] else 1)
+    print(json.dumps({
+        "metric": "stochastic tree acceptance (residual walk over V): verified nodes/s",
+        "value": B * N / t_s, "unit": "nodes/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": t_s * 1e3, "higher_is_better": True,
+        "dtype": "f64", "data": "synthetic",
+        "config": {"workload": f"B={B} requests, N={N}-node random trees, V={V} float32 "
+                               "target and drafter distributions (softmax of N(0,9) logits), "
+                               "children drawn from their parent's drafter row",
+                   "mean_accepted": float(na.float().mean())},
+        "roofline": {"bound": "hbm", "achieved": sbytes / t_s / 1e9, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": sbytes / t_s / 1e9 / HBM_PEAK_GBS,
+                     "traffic": None, "kernel": "tv_stochastic_walk_kernel",
+                     "kernel_p10_p50_p90_us": pct_s, "algorithmic_bytes_per_launch": sbytes},
+        "parity": {"requests": [0, B - 1], "ok": bool(ok_s)}}), flush=True)
+    del p, q
 
     # ---- compaction on the headline cache ----
     L = np.full(B, Lp, np.int32)

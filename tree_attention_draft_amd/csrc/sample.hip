@@ -10,6 +10,9 @@
 // with z_j the total of r_j, so every test costs one pass over the node's p and q rows
 // (the total of the residual a rejection leaves is the next test's z) and the final draw
 // two.  All arithmetic is float64, every reduction in one fixed order per launch shape.
+// Each level divides by its total as one multiply-add with the total's reciprocal (one
+// division per level, not per entry), which differs from a division by at most an ulp,
+// the order of the differences the summation order already makes.
 #include <climits>
 
 #include "kernels_common.h"
@@ -50,21 +53,47 @@ __device__ int block_extreme(int v, int* red) {
   return t;
 }
 
-// r_k at one vocabulary entry from its p and q values and the k divisors applied so far.
-__device__ inline double residual_at(float pv, float qv, const double* zs, int levels) {
+// r_k at one vocabulary entry from its p and q values and the reciprocals of the k totals
+// applied so far.
+__device__ inline double residual_at(float pv, float qv, const double* inv, int levels) {
   double r = static_cast<double>(pv);
   const double qd = static_cast<double>(qv);
-  for (int j = 0; j < levels; ++j) r = fmax(r / zs[j] - qd, 0.0);
+  for (int j = 0; j < levels; ++j) r = fmax(fma(r, inv[j], -qd), 0.0);
   return r;
+}
+
+// Loads per thread issued together before any of them is used (the per-element arithmetic
+// holds a loop of runtime length, so the compiler would otherwise wait a memory round
+// trip per element).
+constexpr int kBatch = 8;
+constexpr int kDraw = 8;  // consecutive entries per thread in the final draw's tiles
+
+// This thread's sum of f(p[v], q[v]) over v = tid, tid + 1024, ... (in that order).
+template <bool NEED_Q, class F>
+__device__ double strided_sum(const float* prow, const float* qrow, int V, F f) {
+  double acc = 0.0;
+  for (int base = threadIdx.x; base < V; base += kWalkThreads * kBatch) {
+    float pv[kBatch], qv[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int v = base + i * kWalkThreads;
+      pv[i] = v < V ? prow[v] : 0.f;
+      qv[i] = NEED_Q && v < V ? qrow[v] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+      if (base + i * kWalkThreads < V) acc += f(pv[i], qv[i]);
+  }
+  return acc;
 }
 
 __global__ void __launch_bounds__(kWalkThreads) tv_stochastic_walk_kernel(SampleParams P) {
   __shared__ int32_t par[TV_MAX_NODES], tok[TV_MAX_NODES];
   __shared__ int32_t acc[TV_MAX_NODES], em[TV_MAX_NODES];
-  __shared__ double zs[TV_MAX_NODES];  // divisors of the current node's applied rejections
+  __shared__ double zs[TV_MAX_NODES];  // 1 / total of each applied rejection's r
   __shared__ double red[kWalkWaves];
   __shared__ int ired[kWalkWaves];
-  __shared__ double scan[kWalkThreads];
+  __shared__ double scan[kWalkWaves];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int N = P.N, V = P.V;
@@ -84,10 +113,9 @@ __global__ void __launch_bounds__(kWalkThreads) tv_stochastic_walk_kernel(Sample
     const float* prow = P.p + (int64_t)b * P.p_sb + (int64_t)node * P.p_sn;
     const float* qrow = P.q + (int64_t)b * P.q_sb + (int64_t)node * P.q_sn;
     int levels = 0;
-    double part = 0.0;
-#pragma unroll 8
-    for (int v = tid; v < V; v += kWalkThreads) part += static_cast<double>(prow[v]);
-    double z = block_sum(part, red);  // total of r_0 = p
+    double z = block_sum(strided_sum<false>(prow, qrow, V,
+                                            [](float pv, float) { return static_cast<double>(pv); }),
+                         red);  // total of r_0 = p
     int taken = -1;
     for (int c = node + 1; c < N; ++c) {
       if (par[c] != node) continue;
@@ -99,15 +127,18 @@ __global__ void __launch_bounds__(kWalkThreads) tv_stochastic_walk_kernel(Sample
         break;
       }
       // rejected: the residual's total decides whether it replaces r
-      double m = 0.0;
-#pragma unroll 4
-      for (int v = tid; v < V; v += kWalkThreads)
-        m += fmax(residual_at(prow[v], qrow[v], zs, levels) / z - static_cast<double>(qrow[v]),
-                  0.0);
-      m = block_sum(m, red);
+      const double iz = 1.0 / z;
+      const double m = block_sum(
+          strided_sum<true>(prow, qrow, V,
+                            [&](float pv, float qv) {
+                              return fmax(fma(residual_at(pv, qv, zs, levels), iz,
+                                              -static_cast<double>(qv)),
+                                          0.0);
+                            }),
+          red);
       if (m > 0.0) {
         __syncthreads();  // every thread is done reading zs[0 .. levels)
-        if (tid == 0) zs[levels] = z;
+        if (tid == 0) zs[levels] = iz;
         __syncthreads();
         ++levels;
         z = m;
@@ -120,39 +151,61 @@ __global__ void __launch_bounds__(kWalkThreads) tv_stochastic_walk_kernel(Sample
       node = taken;
       continue;
     }
-    // ---- final draw from r by inverse CDF: thread tid owns a contiguous chunk ----
-    const int chunk = (V + kWalkThreads - 1) / kWalkThreads;
-    const int v0 = min(V, tid * chunk), v1 = min(V, v0 + chunk);
-    double s = 0.0;
-    int lastpos = -1;
-    for (int v = v0; v < v1; ++v) {
-      const double r = residual_at(prow[v], qrow[v], zs, levels);
-      s += r;
-      if (r > 0.0) lastpos = v;
-    }
-    __syncthreads();
-    scan[tid] = s;
-    __syncthreads();
-    // inclusive scan of the chunk totals (Hillis-Steele, fixed order)
-    for (int off = 1; off < kWalkThreads; off <<= 1) {
-      const double add = tid >= off ? scan[tid - off] : 0.0;
-      __syncthreads();
-      scan[tid] += add;
-      __syncthreads();
-    }
-    const double total = scan[kWalkThreads - 1];
-    const double thresh = u[0] * total;
-    double run = tid > 0 ? scan[tid - 1] : 0.0;
-    int first = INT_MAX;
-    for (int v = v0; v < v1; ++v) {
-      run += residual_at(prow[v], qrow[v], zs, levels);
-      if (run > thresh) {
-        first = v;
-        break;
+    // ---- final draw from r by inverse CDF.  z is r's total; the running sum is walked
+    // in tiles of kDraw * 1024 consecutive entries (kDraw per thread, loads coalesced),
+    // each scanned across the workgroup, until the tile where it exceeds z * uniform[0] ----
+    const double thresh = u[0] * z;
+    double base = 0.0;  // running sum before the current tile
+    int first = INT_MAX, lastpos = -1;
+    for (int t0 = 0; t0 < V; t0 += kWalkThreads * kDraw) {
+      const int v0 = t0 + tid * kDraw;
+      float pv[kDraw], qv[kDraw];
+#pragma unroll
+      for (int i = 0; i < kDraw; ++i) {
+        pv[i] = v0 + i < V ? prow[v0 + i] : 0.f;
+        qv[i] = levels > 0 && v0 + i < V ? qrow[v0 + i] : 0.f;
       }
+      double r[kDraw];
+      double own = 0.0;
+#pragma unroll
+      for (int i = 0; i < kDraw; ++i) {
+        r[i] = v0 + i < V ? residual_at(pv[i], qv[i], zs, levels) : 0.0;
+        own += r[i];
+        if (r[i] > 0.0) lastpos = v0 + i;
+      }
+      // exclusive scan of the threads' sums: within the wave by shuffles, then the waves'
+      // totals in wave order
+      const int lane = tid & 63, w = tid >> 6;
+      double incl = own;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const double y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      const double below = __shfl_up(incl, 1);
+      __syncthreads();  // `scan` is free
+      if (lane == 63) scan[w] = incl;
+      __syncthreads();
+      double before = 0.0, tile = 0.0;
+#pragma unroll
+      for (int j = 0; j < kWalkWaves; ++j) {
+        if (j < w) before += scan[j];
+        tile += scan[j];
+      }
+      if (base + tile > thresh) {  // the same for every thread
+        double run = base + before + (lane > 0 ? below : 0.0);
+        int f = INT_MAX;
+#pragma unroll
+        for (int i = 0; i < kDraw; ++i) {
+          run += r[i];
+          if (f == INT_MAX && run > thresh) f = v0 + i;
+        }
+        first = block_extreme<true>(f, ired);
+        if (first != INT_MAX) break;  // rounding may leave the crossing to the next tile
+      }
+      base += tile;
     }
-    first = block_extreme<true>(first, ired);
-    lastpos = block_extreme<false>(lastpos, ired);
+    if (first == INT_MAX) lastpos = block_extreme<false>(lastpos, ired);
     if (tid == 0) em[a] = first != INT_MAX ? first : lastpos;
     ++a;
     break;
