@@ -8,8 +8,9 @@
 // LDS from the parent array, never read as a dense mask.
 //
 // One workgroup = (key split, kv head x row chunk, request); 4 waves, 4 packed rows each.
-// Keys stream through LDS in 64-key tiles converted to fp32; lane = key for the scores,
-// lane = feature for P.V; online softmax in the exp2 domain with wave reductions.
+// Keys stream through LDS in 64-key tiles converted to fp32 (16-byte loads, all of a tile's
+// issued before any is stored); lane = key for the scores, lane = feature for P.V; online
+// softmax in the exp2 domain with wave reductions.
 #include "kernels_common.h"
 
 namespace tv {
@@ -20,6 +21,26 @@ template <>
 __device__ inline float load_elem<float>(const float* p) { return *p; }
 template <>
 __device__ inline float load_elem<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+
+// The 16-byte chunk `c` (four fp32 or eight bf16 values) unpacked to fp32.
+template <typename T>
+__device__ inline void unpack16(const uint4& c, float* out);
+template <>
+__device__ inline void unpack16<float>(const uint4& c, float* out) {
+  out[0] = __uint_as_float(c.x);
+  out[1] = __uint_as_float(c.y);
+  out[2] = __uint_as_float(c.z);
+  out[3] = __uint_as_float(c.w);
+}
+template <>
+__device__ inline void unpack16<uint16_t>(const uint4& c, float* out) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
 
 template <typename T>
 __device__ inline void store_elem(T* p, float v);
@@ -38,6 +59,7 @@ __global__ void __launch_bounds__(256) tv_attn_valu_kernel(AttnParams p) {
   __shared__ float Vs[KT][D];
   __shared__ float Qs[ROWS][D];
   __shared__ float Ps[4][KT];
+  __shared__ double inv_s[D / 2];  // rotary pair frequencies, formed once per workgroup
   __shared__ uint64_t mask_s[TV_MAX_NODES];
   __shared__ int32_t par_s[TV_MAX_NODES];
 
@@ -80,6 +102,8 @@ __global__ void __launch_bounds__(256) tv_attn_valu_kernel(AttnParams p) {
     }
     Qs[r][d] = val;
   }
+  if (p.rope)
+    for (int i = tid; i < D / 2; i += 256) inv_s[i] = rope_inv_freq(i, D, p.rope_log2_theta);
   __syncthreads();
   if (p.rope) {  // fused rotary embedding of the queries at L + depth (uniform branch)
     for (int idx = tid; idx < ROWS * (D / 2); idx += 256) {
@@ -87,7 +111,7 @@ __global__ void __launch_bounds__(256) tv_attn_valu_kernel(AttnParams p) {
       const int row = rc * ROWS + r;
       if (row >= p.R) continue;
       float cs, sn;
-      rope_cos_sin(L + depth_of(mask_s[row / p.g]), mm, D, p.rope_log2_theta, cs, sn);
+      rope_cos_sin_inv(L + depth_of(mask_s[row / p.g]), inv_s[mm], cs, sn);
       rope_pair(Qs[r][mm], Qs[r][mm + D / 2], cs, sn);
     }
     __syncthreads();
@@ -107,18 +131,37 @@ __global__ void __launch_bounds__(256) tv_attn_valu_kernel(AttnParams p) {
     for (int e = 0; e < E; ++e) o[j][e] = 0.f;
   }
 
+  // a tile's K and V as 16-byte chunks (strides and bases are 16-byte multiples), every
+  // load of the tile issued before any of them is stored to LDS
+  constexpr int VE = 16 / sizeof(T);            // elements per chunk
+  constexpr int CPR = D / VE;                   // chunks per row
+  constexpr int PER = KT * CPR / 256;           // chunks per thread, K and V each
+  static_assert(KT * CPR % 256 == 0, "tile chunks split evenly over the workgroup");
   for (int kt0 = kbeg; kt0 < kend; kt0 += KT) {
-    for (int idx = tid; idx < KT * D; idx += 256) {
-      const int key = idx / D, d = idx - (idx / D) * D;
-      const int t = kt0 + key;
-      float kv = 0.f, vv = 0.f;
+    uint4 kc[PER], vc[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = tid + 256 * i;
+      const int t = kt0 + c / CPR;
+      kc[i] = vc[i] = make_uint4(0, 0, 0, 0);
       if (t < kend) {
-        const int64_t off = kv_offset(p, b, t, hkv) + d;
-        kv = load_elem<T>(kp + off);
-        vv = load_elem<T>(vp + off);
+        const int64_t off = kv_offset(p, b, t, hkv) + (c % CPR) * VE;
+        kc[i] = *reinterpret_cast<const uint4*>(kp + off);
+        vc[i] = *reinterpret_cast<const uint4*>(vp + off);
       }
-      Ks[key][d] = kv;
-      Vs[key][d] = vv;
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = tid + 256 * i;
+      const int key = c / CPR, d0 = (c % CPR) * VE;
+      float kf[VE], vf[VE];
+      unpack16<T>(kc[i], kf);
+      unpack16<T>(vc[i], vf);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        Ks[key][d0 + e] = kf[e];
+        Vs[key][d0 + e] = vf[e];
+      }
     }
     __syncthreads();
     if (p.rope && kt0 + KT > L) {  // tile holds tree keys: rotate them at L + depth
@@ -127,7 +170,7 @@ __global__ void __launch_bounds__(256) tv_attn_valu_kernel(AttnParams p) {
         const int t = kt0 + key;
         if (t < L || t >= kend) continue;
         float cs, sn;
-        rope_cos_sin(L + depth_of(mask_s[t - L]), mm, D, p.rope_log2_theta, cs, sn);
+        rope_cos_sin_inv(L + depth_of(mask_s[t - L]), inv_s[mm], cs, sn);
         rope_pair(Ks[key][mm], Ks[key][mm + D / 2], cs, sn);
       }
       __syncthreads();
