@@ -200,6 +200,13 @@ tv_status make_plan(const tv_attn_args* a, Plan* pl) {
     const int64_t cus = device_cu_count();
     if (S * a->Hkv * pl->row_chunks * (int64_t)a->B == 2 * cus) pl->young_from = (int)cus;
   }
+  // A grid of at most one workgroup per compute unit (small batches) would leave each SIMD
+  // a single wave: the four-wave shapes then run two teams of four waves per workgroup,
+  // splitting every window's tiles (D = 128, no fused rotary embedding).
+  if (pl->mfma && a->D == 128 && !(a->rope_theta > 0.0) && pl->shape.nw == 4) {
+    const int64_t wgs = S * a->Hkv * pl->row_chunks * (int64_t)a->B;
+    if (wgs <= device_cu_count()) pl->shape.teams = 2;
+  }
   if (S > 1) {
     const size_t rows = (size_t)a->B * a->Hkv * S * R;
     pl->ws_o_bytes = rows * a->D * sizeof(float);

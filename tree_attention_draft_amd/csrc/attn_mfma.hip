@@ -359,11 +359,18 @@ __device__ inline void rope_q_tile(bf16x8 (&q)[D / 32], char* slot, const float2
 // across the g heads (row = (node - 16*TN) * g + head), computed by wave it % NW on key
 // tile `it`; each wave keeps its own online-softmax partial of that tile and the partials
 // are merged through LDS at the end (the same maths as the split merge).
-template <int D, int KT, int NST, int TN, int RR, int NW, bool ROPE>
-__global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) {
+// TEAMS = 2 (grids of at most one workgroup per compute unit): two teams of NW waves, so
+// each SIMD holds a wave of each; every window of 2 * TEAMS key tiles gives each team two
+// of them, and at the end team 1's online-softmax partials merge into team 0's through
+// LDS.  One prologue and one partial per workgroup, as with one team.
+template <int D, int KT, int NST, int TN, int RR, int NW, bool ROPE, int TEAMS>
+__global__ void __launch_bounds__(NW * 64 * TEAMS, TEAMS == 1 ? 2 : 1)
+    tv_attn_mfma_kernel(AttnParams p) {
   using C = MfmaCfg<D, KT, NST, TN, NW>;
   constexpr int DS = C::DS, DB = C::DB, KB = C::KB, KS = C::KS;
   constexpr int TT = TN + RR;  // tiles of state per wave: full tiles, then the shared one
+  constexpr int NTH = NW * 64 * TEAMS;  // threads of the workgroup
+  static_assert(TEAMS == 1 || (TEAMS == 2 && !ROPE), "teams: the plain pass only");
   __shared__ __attribute__((aligned(1024))) char smem[NST * C::STAGEB];
   __shared__ uint64_t mask_s[TV_MAX_NODES];
   __shared__ int32_t par_s[TV_MAX_NODES];
@@ -373,12 +380,16 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
   __shared__ bf16x8 qrem_s[RR ? DS * 64 : 1];
   // rotary pair frequencies, formed once in fp64 (fused RoPE only)
   __shared__ double inv_s[ROPE ? D / 2 : 1];
-  static_assert(!RR || NW * 16 * D * 4 <= NST * C::STAGEB, "merge buffer fits the ring");
-  static_assert(!RR || NW * 16 * 2 <= kMaxPageSlice, "merge (m, l) fits the page slice");
+  static_assert(!RR || TEAMS * NW * 16 * D * 4 <= NST * C::STAGEB, "merge buffer fits the ring");
+  static_assert(!RR || TEAMS * NW * 16 * 2 <= kMaxPageSlice, "merge (m, l) fits the page slice");
+  static_assert(TEAMS == 1 || NW * TN * DB * 64 * 16 + NW * TN * 64 * 8 <= NST * C::STAGEB,
+                "team merge buffer fits the ring");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave of the workgroup
+  const int team = TEAMS == 1 ? 0 : wv / NW;                // 0 unless TEAMS == 2
+  const int w = TEAMS == 1 ? wv : wv - team * NW;           // wave within its team
   const int lr = lane & 15;
   const int lh = lane >> 4;
   const int hkv = blockIdx.y % p.Hkv;
@@ -387,7 +398,7 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
   static_assert(3 * kMaxLptBatch + 1 <= kMaxPageSlice, "piece order fits the page slice");
   int b = blockIdx.z, split = blockIdx.x;
   if (p.lpt) {
-    if (!lpt_piece(p, blockIdx.z * gridDim.x + blockIdx.x, pt_s, tid, NW * 64, b, split))
+    if (!lpt_piece(p, blockIdx.z * gridDim.x + blockIdx.x, pt_s, tid, NTH, b, split))
       return;  // more slots than pieces
     b = __builtin_amdgcn_readfirstlane(b);
     split = __builtin_amdgcn_readfirstlane(split);
@@ -462,7 +473,7 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
     rm.pbase = p.page_shift >= 0 ? (kbeg >> p.page_shift) : kbeg / p.page_size;
     const int plast = p.page_shift >= 0 ? ((kend - 1) >> p.page_shift) : (kend - 1) / p.page_size;
     const int32_t* prow = p.page_table + (int64_t)b * p.pages_per_seq;
-    for (int i = tid; i <= plast - rm.pbase; i += NW * 64) pt_s[i] = prow[rm.pbase + i];
+    for (int i = tid; i <= plast - rm.pbase; i += NTH) pt_s[i] = prow[rm.pbase + i];
   } else {
     rm.head_off = (int64_t)b * p.kv_sb + (int64_t)hkv * p.kv_sh;
   }
@@ -483,7 +494,7 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
     float2* cs_tab = reinterpret_cast<float2*>(smem + NW * DS * 1024);
     if (tid < H) inv_s[tid] = rope_inv_freq(tid, D, p.rope_log2_theta);
     __syncthreads();
-    for (int idx = tid; idx < nrows * H; idx += NW * 64) {
+    for (int idx = tid; idx < nrows * H; idx += NTH) {
       const int i = idx / H, m = idx - (idx / H) * H;
       float cs, sn;
       rope_cos_sin_inv(L + depth_of(mask_s[nbase + i]), inv_s[m], cs, sn);
@@ -503,21 +514,24 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
   // ---- park the remainder tile's query operands in LDS ----
   const float c = p.scale_log2;
   if constexpr (RR) {
-    if (w == 0) {
+    if (wv == 0) {
 #pragma unroll
       for (int s = 0; s < DS; ++s) qrem_s[s * 64 + lane] = qreg[TN][s];
     }
     __syncthreads();  // qrem_s visible before the first remainder tile
   }
 
-  // ---- start the first two windows streaming ----
+  // ---- start the first two windows streaming (each team loads its own tiles) ----
+  constexpr int WIN = 2;           // tiles a team computes per window
+  constexpr int SW = WIN * TEAMS;  // tiles per window of the workgroup
+  static_assert(NST == 2 * SW, "a ring of two windows");
   const LoadPlan<C, NW> lp(p, w, lane);
   const bool off32 = (int64_t)(KT - 1) * p.kv_st * 2 + 2 * D <= INT32_MAX;
   const bool fast = !p.paged && off32;
   const bool pfast = p.paged && off32 && p.page_shift >= 0 && p.page_size % C::RPI == 0;
 #pragma unroll
   for (int s = 0; s < NST; ++s)
-    if (s < ntiles)
+    if (s < ntiles && (s / WIN) % TEAMS == team)
       issue_tile<C, NW, KT>(p, rm, lp, kg, vg, sbase + s * C::STAGEB, kbeg + s * KT, kend, fast,
                             pfast, w, lane);
 
@@ -533,8 +547,11 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
     for (int db = 0; db < DB; ++db) o[t][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // One key tile: S^T = K Q^T, mask, online softmax, O^T += V^T P^T.
-  auto tile = [&](int it, bool do_rem, auto young_c) {
+  // One key tile: S^T = K Q^T, mask, online softmax, O^T += V^T P^T.  `it` is the tile's
+  // index in the split, `k` its index among the tiles this wave's team computes (the same
+  // with one team): a row tile's first tile, k == 0, and the remainder tile's first
+  // (k < NW) take the exact step.
+  auto tile = [&](int it, int k, bool do_rem, auto young_c) {
     constexpr bool young = decltype(young_c)::value;
     const int kt0 = kbeg + it * KT;
     const char* ks = smem + (it % NST) * C::STAGEB;
@@ -580,7 +597,7 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
       if (t >= TN && !do_rem) continue;
       // a full tile's first key tile is the split's first; the remainder tile's is the
       // first this wave computes (it < NW)
-      const bool exact = masked || (t < TN ? it == 0 : it < NW);
+      const bool exact = masked || (t < TN ? k == 0 : k < NW);
       if (exact) {
         if (masked) apply_mask<KB>(sacc[t], tile_allowed(mask_s[node_of[t]], kt0, L) >> (4 * lh));
         rebase_exact<KB, DB>(sacc[t], c, m[t], nm4[t], l[t], o[t]);
@@ -592,7 +609,7 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
 #pragma unroll
       for (int t = 0; t < TT; ++t) {
         if (t >= TN && !do_rem) continue;
-        if (masked || (t < TN ? it == 0 : it < NW)) continue;
+        if (masked || (t < TN ? k == 0 : k < NW)) continue;
         if (__any(!(lt[t] <= kTripSum))) {
           rebase_exact<KB, DB>(sacc[t], c, m[t], nm4[t], l[t], o[t]);
           lt[t] = exp_pack<KB, KS>(sacc[t], c, pk[t]);
@@ -640,26 +657,32 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
     mfma_priority(false, young);
   };
 
-  // Tiles go in windows of WIN = NST/2: one barrier per window publishes its WIN tiles and
+  // Tiles go in windows of SW = TEAMS * WIN: one barrier per window publishes its tiles and
   // frees the stages of the previous window, whose loads for the next window then stream
-  // while this one is computed.  The shared remainder tile of key tile `it` is computed by
-  // wave it % NW, so within a window the extra work lands on WIN different waves.
-  constexpr int WIN = NST / 2;
+  // while this one is computed; team t computes (and loads) tiles t*WIN .. t*WIN+WIN-1 of
+  // every window.  The shared remainder tile of a key tile is computed by wave k % NW of
+  // the team that has the tile, k the tile's index among that team's tiles, so within a
+  // window the extra work lands on WIN different waves of each team.
   // The loop is compiled twice, for the older and the younger workgroup of a unit, so the
   // priority switches inside the tiles take no branch.
   auto key_loop = [&](auto young_c) {
-    for (int it = 0; it < ntiles; it += WIN) {
+    const int own = team * WIN;  // this team's first tile within a window
+    for (int it = 0; it < ntiles; it += SW) {
       if (it == 0) {
-        // the prologue issued tiles 0 .. min(NST, ntiles)-1; tiles of window 1 may remain
-        wait_tiles<C::LPW, WIN>(min(ntiles, NST) - min(ntiles, WIN));
+        // the prologue issued this team's tiles of windows 0 and 1; those of window 1 may
+        // remain in flight
+        if constexpr (TEAMS == 1)
+          wait_tiles<C::LPW, WIN>(min(ntiles, NST) - min(ntiles, WIN));
+        else
+          wait_tiles<C::LPW, WIN>(max(0, min(ntiles - SW - own, WIN)));
       } else {
-        wait_vmcnt<0>();  // this window's tiles were the last ones issued
+        wait_vmcnt<0>();  // this window's tiles were the last ones this wave issued
       }
       __syncthreads();  // window visible to all waves; the previous window's stages are free
       if (it > 0) {
 #pragma unroll
         for (int s = 0; s < WIN; ++s) {
-          const int tn = it + WIN + s;
+          const int tn = it + SW + own + s;
           if (tn < ntiles)
             issue_tile<C, NW, KT>(p, rm, lp, kg, vg, sbase + (tn % NST) * C::STAGEB,
                                   kbeg + tn * KT, kend, fast, pfast, w, lane);
@@ -677,12 +700,13 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
       if (!head_on) continue;  // surplus wave of a group smaller than NW: loads only
 #pragma unroll
       for (int s = 0; s < WIN; ++s) {
-        const int tt = it + s;
-        if (tt < ntiles) tile(tt, RR && (tt % NW) == w, young_c);
+        const int tt = it + own + s;
+        const int k = TEAMS == 1 ? tt : it / TEAMS + s;  // this team's tile count so far
+        if (tt < ntiles) tile(tt, k, RR && (k % NW) == w, young_c);
       }
     }
   };
-  if constexpr (NW == 4 && TN <= 2) {  // the shapes the host may flag (three-tile waves
+  if constexpr (NW == 4 && TN <= 2 && TEAMS == 1) {  // the shapes the host may flag (three-tile waves
                                        // would spill with two copies of the loop)
     if ((int)((blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) >= p.young_from)
       key_loop(std::true_type{});
@@ -692,8 +716,40 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
     key_loop(std::false_type{});
   }
 
+  if constexpr (TEAMS == 2) {
+    // ---- team 1's partials of the full tiles merge into team 0's through LDS ----
+    f32x4* xo = reinterpret_cast<f32x4*>(smem);                        // [NW][TN][DB][64]
+    float* xm = reinterpret_cast<float*>(smem + NW * TN * DB * 64 * 16);  // [NW][TN][64] x (m, l)
+    __syncthreads();  // every wave is done with the ring
+    if (team == 1 && head_on) {
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) xo[((w * TN + t) * DB + db) * 64 + lane] = o[t][db];
+        xm[((w * TN + t) * 64 + lane) * 2] = m[t];
+        xm[((w * TN + t) * 64 + lane) * 2 + 1] = l[t];
+      }
+    }
+    __syncthreads();
+    if (team == 0 && head_on) {
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        const float m1 = xm[((w * TN + t) * 64 + lane) * 2];
+        const float l1 = xm[((w * TN + t) * 64 + lane) * 2 + 1];
+        const float mx = fmaxf(m[t], m1);
+        const float s0 = m[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[t] - mx);
+        const float s1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mx);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          o[t][db] = o[t][db] * s0 + xo[((w * TN + t) * DB + db) * 64 + lane] * s1;
+        l[t] = l[t] * s0 + l1 * s1;
+        m[t] = mx;
+      }
+    }
+  }
+
   // ---- epilogue: full tiles straight from registers ----
-  if (head_on) {
+  if (head_on && team == 0) {
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
       float lt = l[t];
@@ -707,32 +763,32 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
   }
   if constexpr (RR) {
     // ---- shared remainder tile: merge the waves' partials through LDS ----
-    float* mo = reinterpret_cast<float*>(smem);   // [NW][16][D] unnormalised O
-    float* ml = reinterpret_cast<float*>(pt_s);   // [NW][16] x (m, l)
+    float* mo = reinterpret_cast<float*>(smem);   // [TEAMS * NW][16][D] unnormalised O
+    float* ml = reinterpret_cast<float*>(pt_s);   // [TEAMS * NW][16] x (m, l)
     __syncthreads();                              // every wave is done with the ring
     float lt = l[TN];
     lt += __shfl_xor(lt, 16);
     lt += __shfl_xor(lt, 32);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-      *reinterpret_cast<f32x4*>(mo + (w * 16 + lr) * D + db * 16 + 4 * lh) = o[TN][db];
+      *reinterpret_cast<f32x4*>(mo + (wv * 16 + lr) * D + db * 16 + 4 * lh) = o[TN][db];
     if (lh == 0) {
-      ml[(w * 16 + lr) * 2] = head_on ? m[TN] : -INFINITY;
-      ml[(w * 16 + lr) * 2 + 1] = head_on ? lt : 0.f;
+      ml[(wv * 16 + lr) * 2] = head_on ? m[TN] : -INFINITY;
+      ml[(wv * 16 + lr) * 2 + 1] = head_on ? lt : 0.f;
     }
     __syncthreads();
-    for (int item = tid; item < 16 * (D / 4); item += NW * 64) {
+    for (int item = tid; item < 16 * (D / 4); item += NTH) {
       const int row = item / (D / 4);
       const int q4 = item % (D / 4);
       if (row >= rem_rows) continue;
       float M = -INFINITY;
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, ml[(ww * 16 + row) * 2]);
+      for (int ww = 0; ww < TEAMS * NW; ++ww) M = fmaxf(M, ml[(ww * 16 + row) * 2]);
       float Ls = 0.f;
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
       if (M != -INFINITY) {
 #pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
+        for (int ww = 0; ww < TEAMS * NW; ++ww) {
           const float mw = ml[(ww * 16 + row) * 2];
           if (mw == -INFINITY) continue;
           const float sc = __builtin_amdgcn_exp2f(mw - M);
@@ -765,27 +821,35 @@ __global__ void __launch_bounds__(NW * 64, 2) tv_attn_mfma_kernel(AttnParams p) 
 constexpr int kMfmaKT = 32;
 constexpr int kMfmaNST = 4;
 
-template <int D, bool ROPE>
+template <int D, bool ROPE, int TEAMS>
 static hipError_t launch_d(const AttnParams& p, MfmaShape sh, hipStream_t s) {
   dim3 grid(p.num_splits, p.Hkv * p.row_chunks, p.B);
-#define TV_CASE(TN, RR, NW)                                                               \
-  if (sh.tpw == TN && sh.rr == RR && sh.nw == NW) {                                       \
-    hipLaunchKernelGGL((tv_attn_mfma_kernel<D, kMfmaKT, kMfmaNST, TN, RR, NW, ROPE>),     \
-                       grid, dim3(NW * 64), 0, s, p);                                     \
-    return hipGetLastError();                                                             \
+#define TV_CASE(TN, RR, NW)                                                                  \
+  if (sh.tpw == TN && sh.rr == RR && sh.nw == NW) {                                          \
+    hipLaunchKernelGGL(                                                                      \
+        (tv_attn_mfma_kernel<D, kMfmaKT, kMfmaNST * TEAMS, TN, RR, NW, ROPE, TEAMS>), grid, \
+        dim3(NW * 64 * TEAMS), 0, s, p);                                                     \
+    return hipGetLastError();                                                                \
   }
-  TV_CASE(1, 0, 1) TV_CASE(1, 0, 2) TV_CASE(1, 0, 4) TV_CASE(1, 0, 8)
-  TV_CASE(2, 0, 1) TV_CASE(2, 0, 2) TV_CASE(2, 0, 4) TV_CASE(2, 0, 8)
-  TV_CASE(3, 0, 1) TV_CASE(3, 0, 2) TV_CASE(3, 0, 4) TV_CASE(3, 0, 8)
-  TV_CASE(1, 1, 2) TV_CASE(1, 1, 4) TV_CASE(1, 1, 8)
-  TV_CASE(2, 1, 2) TV_CASE(2, 1, 4) TV_CASE(2, 1, 8)
+  if constexpr (TEAMS == 2) {  // four-wave groups only (the host flags no others)
+    TV_CASE(1, 0, 4) TV_CASE(2, 0, 4) TV_CASE(3, 0, 4) TV_CASE(1, 1, 4) TV_CASE(2, 1, 4)
+    return hipErrorInvalidConfiguration;
+  } else {
+    TV_CASE(1, 0, 1) TV_CASE(1, 0, 2) TV_CASE(1, 0, 4) TV_CASE(1, 0, 8)
+    TV_CASE(2, 0, 1) TV_CASE(2, 0, 2) TV_CASE(2, 0, 4) TV_CASE(2, 0, 8)
+    TV_CASE(3, 0, 1) TV_CASE(3, 0, 2) TV_CASE(3, 0, 4) TV_CASE(3, 0, 8)
+    TV_CASE(1, 1, 2) TV_CASE(1, 1, 4) TV_CASE(1, 1, 8)
+    TV_CASE(2, 1, 2) TV_CASE(2, 1, 4) TV_CASE(2, 1, 8)
+  }
 #undef TV_CASE
   return hipErrorInvalidConfiguration;
 }
 
 hipError_t launch_attn_mfma(const AttnParams& p, int D, MfmaShape shape, hipStream_t s) {
-  if (p.rope) return D == 64 ? launch_d<64, true>(p, shape, s) : launch_d<128, true>(p, shape, s);
-  return D == 64 ? launch_d<64, false>(p, shape, s) : launch_d<128, false>(p, shape, s);
+  if (p.rope)
+    return D == 64 ? launch_d<64, true, 1>(p, shape, s) : launch_d<128, true, 1>(p, shape, s);
+  if (D == 128 && shape.teams == 2) return launch_d<128, false, 2>(p, shape, s);
+  return D == 64 ? launch_d<64, false, 1>(p, shape, s) : launch_d<128, false, 1>(p, shape, s);
 }
 
 }  // namespace tv

@@ -61,6 +61,7 @@ struct AttnParams {
 // registers), each streaming the same keys.
 struct MfmaShape {
   int tpw, nw, rr, nc;
+  int teams = 1;  // 2: two teams of nw waves per workgroup (D = 128, nw = 4, no RoPE)
 };
 
 // Device-side arguments of the acceptance kernels (argmax over the vocabulary, walk).
