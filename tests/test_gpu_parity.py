@@ -186,6 +186,20 @@ def test_node_count_sweep(N):
     c.check(out, lse)
 
 
+# Small grids (at most one workgroup per compute unit) run the two-team build: every
+# four-wave shape -- one, two or three 16-node tiles per wave, with and without the shared
+# remainder tile -- over key ranges of 1 to 9 tiles, so a window is often half empty or
+# one team has no tile at all, with and without forced splits (several 32-key tiles per
+# split, and splits of one chunk).
+@pytest.mark.parametrize("N", [10, 17, 32, 33, 48])
+@pytest.mark.parametrize("splits", [0, 3])
+def test_two_team_shapes(N, splits):
+    paths, _ = random_trees(900 + N, 4, N, 8)
+    c = Case(f"teams_n{N}_s{splits}", [0, 20, 97, 240], trees=paths, seed=1500 + N)
+    out, lse = c.run(num_splits=splits)
+    c.check(out, lse)
+
+
 @pytest.mark.parametrize("hq,hkv", [(64, 4), (16, 8), (8, 1)])
 def test_group_sizes_n33(hq, hkv):
     # g = 16 (two head chunks of 8 waves), g = 2, g = 8 with one kv head
