@@ -135,3 +135,23 @@ def test_empty_batch():
         torch.tensor([-1, 0, 0, 1], dtype=torch.int32, device="cuda"),
         torch.zeros((0, 4), dtype=torch.float64, device="cuda"))
     assert acc.shape == (0, 4) and na.shape == (0,)
+
+
+def test_strided_rows_with_a_tail():
+    # rows 16-byte aligned (stride 1004 entries) but V = 1001: the grouped loads take the
+    # first 1000 entries of each row and the tail entry is read on its own
+    import torch
+    B, N, V, W = 6, 14, 1001, 1004
+    parents, p, q, tokens, u = make_inputs(7600, B, N, V)
+    wp = np.zeros((B, N, W), np.float32)
+    wq = np.zeros((B, N, W), np.float32)
+    wp[..., :V], wq[..., :V] = p, q
+    dev = "cuda"
+    tp = torch.from_numpy(wp).to(dev)[..., :V]
+    tq = torch.from_numpy(wq).to(dev)[..., :V]
+    assert tp.stride(1) == W
+    acc, em, na = tv.tree_accept_stochastic(
+        tp, tq, torch.from_numpy(tokens).to(dev),
+        torch.tensor(np.array(parents, np.int32), device=dev), torch.from_numpy(u).to(dev))
+    torch.cuda.synchronize()
+    check(parents, p, q, tokens, u, acc.cpu().numpy(), em.cpu().numpy(), na.cpu().numpy())

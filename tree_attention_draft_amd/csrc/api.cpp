@@ -493,6 +493,8 @@ extern "C" tv_status tree_accept_stochastic(const tv_sample_args* a, hipStream_t
   if (st != TV_OK) return st;
   if (a->B == 0) return TV_OK;
   SampleParams p;
+  p.vec = aligned16(a->p) && aligned16(a->q) && a->p_sb % 4 == 0 && a->p_sn % 4 == 0 &&
+          a->q_sb % 4 == 0 && a->q_sn % 4 == 0;
   p.B = a->B;
   p.N = a->N;
   p.V = a->V;

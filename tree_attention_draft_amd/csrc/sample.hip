@@ -68,10 +68,39 @@ __device__ inline double residual_at(float pv, float qv, const double* inv, int 
 constexpr int kBatch = 8;
 constexpr int kDraw = 8;  // consecutive entries per thread in the final draw's tiles
 
-// This thread's sum of f(p[v], q[v]) over v = tid, tid + 1024, ... (in that order).
-template <bool NEED_Q, class F>
+constexpr int kGroups = 4;  // 16-byte groups per thread issued together (aligned rows)
+
+// This thread's sum of f(p[v], q[v]) over its share of the row, in a fixed order: aligned
+// rows (VEC) by groups of four entries, g = tid, tid + 1024, ..., then the tail entries
+// past the last whole group; otherwise v = tid, tid + 1024, ...
+template <bool VEC, bool NEED_Q, class F>
 __device__ double strided_sum(const float* prow, const float* qrow, int V, F f) {
   double acc = 0.0;
+  if constexpr (VEC) {
+    const int V4 = V >> 2;
+    const float4* p4 = reinterpret_cast<const float4*>(prow);
+    const float4* q4 = reinterpret_cast<const float4*>(qrow);
+    for (int base = threadIdx.x; base < V4; base += kWalkThreads * kGroups) {
+      float4 pv[kGroups], qv[kGroups];
+#pragma unroll
+      for (int i = 0; i < kGroups; ++i) {
+        const int g = base + i * kWalkThreads;
+        pv[i] = g < V4 ? p4[g] : make_float4(0.f, 0.f, 0.f, 0.f);
+        qv[i] = NEED_Q && g < V4 ? q4[g] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int i = 0; i < kGroups; ++i)
+        if (base + i * kWalkThreads < V4) {
+          acc += f(pv[i].x, qv[i].x);
+          acc += f(pv[i].y, qv[i].y);
+          acc += f(pv[i].z, qv[i].z);
+          acc += f(pv[i].w, qv[i].w);
+        }
+    }
+    const int v = 4 * V4 + (int)threadIdx.x;
+    if (v < V) acc += f(prow[v], NEED_Q ? qrow[v] : 0.f);
+    return acc;
+  }
   for (int base = threadIdx.x; base < V; base += kWalkThreads * kBatch) {
     float pv[kBatch], qv[kBatch];
 #pragma unroll
@@ -87,6 +116,7 @@ __device__ double strided_sum(const float* prow, const float* qrow, int V, F f) 
   return acc;
 }
 
+template <bool VEC>
 __global__ void __launch_bounds__(kWalkThreads) tv_stochastic_walk_kernel(SampleParams P) {
   __shared__ int32_t par[TV_MAX_NODES], tok[TV_MAX_NODES];
   __shared__ int32_t acc[TV_MAX_NODES], em[TV_MAX_NODES];
@@ -113,7 +143,7 @@ __global__ void __launch_bounds__(kWalkThreads) tv_stochastic_walk_kernel(Sample
     const float* prow = P.p + (int64_t)b * P.p_sb + (int64_t)node * P.p_sn;
     const float* qrow = P.q + (int64_t)b * P.q_sb + (int64_t)node * P.q_sn;
     int levels = 0;
-    double z = block_sum(strided_sum<false>(prow, qrow, V,
+    double z = block_sum(strided_sum<VEC, false>(prow, qrow, V,
                                             [](float pv, float) { return static_cast<double>(pv); }),
                          red);  // total of r_0 = p
     int taken = -1;
@@ -129,7 +159,7 @@ __global__ void __launch_bounds__(kWalkThreads) tv_stochastic_walk_kernel(Sample
       // rejected: the residual's total decides whether it replaces r
       const double iz = 1.0 / z;
       const double m = block_sum(
-          strided_sum<true>(prow, qrow, V,
+          strided_sum<VEC, true>(prow, qrow, V,
                             [&](float pv, float qv) {
                               return fmax(fma(residual_at(pv, qv, zs, levels), iz,
                                               -static_cast<double>(qv)),
@@ -160,10 +190,27 @@ __global__ void __launch_bounds__(kWalkThreads) tv_stochastic_walk_kernel(Sample
     for (int t0 = 0; t0 < V; t0 += kWalkThreads * kDraw) {
       const int v0 = t0 + tid * kDraw;
       float pv[kDraw], qv[kDraw];
+      if (VEC && v0 + kDraw <= V) {  // two 16-byte loads per row (v0 is a multiple of 8)
+        static_assert(kDraw == 8, "draw chunk of two 16-byte groups");
+        const float4 pa = *reinterpret_cast<const float4*>(prow + v0);
+        const float4 pb = *reinterpret_cast<const float4*>(prow + v0 + 4);
+        pv[0] = pa.x; pv[1] = pa.y; pv[2] = pa.z; pv[3] = pa.w;
+        pv[4] = pb.x; pv[5] = pb.y; pv[6] = pb.z; pv[7] = pb.w;
+        if (levels > 0) {
+          const float4 qa = *reinterpret_cast<const float4*>(qrow + v0);
+          const float4 qb = *reinterpret_cast<const float4*>(qrow + v0 + 4);
+          qv[0] = qa.x; qv[1] = qa.y; qv[2] = qa.z; qv[3] = qa.w;
+          qv[4] = qb.x; qv[5] = qb.y; qv[6] = qb.z; qv[7] = qb.w;
+        } else {
 #pragma unroll
-      for (int i = 0; i < kDraw; ++i) {
-        pv[i] = v0 + i < V ? prow[v0 + i] : 0.f;
-        qv[i] = levels > 0 && v0 + i < V ? qrow[v0 + i] : 0.f;
+          for (int i = 0; i < kDraw; ++i) qv[i] = 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kDraw; ++i) {
+          pv[i] = v0 + i < V ? prow[v0 + i] : 0.f;
+          qv[i] = levels > 0 && v0 + i < V ? qrow[v0 + i] : 0.f;
+        }
       }
       double r[kDraw];
       double own = 0.0;
@@ -221,7 +268,10 @@ __global__ void __launch_bounds__(kWalkThreads) tv_stochastic_walk_kernel(Sample
 }  // namespace
 
 hipError_t launch_stochastic_walk(const SampleParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(tv_stochastic_walk_kernel, dim3(p.B), dim3(kWalkThreads), 0, s, p);
+  if (p.vec)
+    hipLaunchKernelGGL(tv_stochastic_walk_kernel<true>, dim3(p.B), dim3(kWalkThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(tv_stochastic_walk_kernel<false>, dim3(p.B), dim3(kWalkThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -83,6 +83,7 @@ struct AcceptParams {
 
 // Device-side arguments of the stochastic walk kernel.
 struct SampleParams {
+  bool vec;  // every p and q row is 16-byte aligned
   int B, N, V;
   const float* p;
   int64_t p_sb, p_sn;
