@@ -336,12 +336,14 @@ def main():
     ap.add_argument("--rope-theta", type=float, default=0.0,
                     help="> 0: time the pass with the rotary embedding fused in")
     ap.add_argument("--after-pass", action="store_true",
-                    help="time greedy acceptance and KV compaction instead (two JSON lines)")
+                    help="time greedy and stochastic acceptance, KV compaction and the budget "
+                         "policy instead (four JSON lines)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}, "
-              f"WORLD_SIZE={world}); multi-GPU sharding is design-only.", file=sys.stderr)
+        print(f"bench.py: the pass runs and is measured on one GPU only (asked for --gpus "
+              f"{args.gpus}, WORLD_SIZE={world}); sharding across GPUs is not implemented.",
+              file=sys.stderr)
         sys.exit(2)
 
     if args.after_pass:
