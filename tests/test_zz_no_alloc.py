@@ -84,3 +84,38 @@ def test_static_entry_point_rejects_oversized_plans_before_enqueueing():
     assert "static scratch" in tv.lib().tv_last_error().decode()
     torch.cuda.synchronize()
     assert bool((out == 3.0).all())       # nothing was enqueued
+
+
+def test_static_entry_point_replays_in_a_captured_graph():
+    # the callers this entry point is for: code under graph capture.  A split plan (so the
+    # static array and the merge kernel are inside the graph) is captured once and replayed
+    # three times, with new queries written eagerly between replays; every replay must
+    # equal an eager tree_verify_attn call on the same inputs bit for bit.
+    c = Case("graph", [600, 333, 97], trees=trees(9200, 3, 33, 8), seed=9200)
+    d = c.device()
+    q, maxl = d["q"], int(c.L.max())
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    kw = dict(out=out, lse=lse, num_splits=3)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # first call outside capture: module load, array address
+        tv.tree_verify_attn_static(q, d["k"], d["v"], d["parent"], d["prefix_len"], maxl, **kw)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        tv.tree_verify_attn_static(q, d["k"], d["v"], d["parent"], d["prefix_len"], maxl, **kw)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(9201)
+    for rep in range(3):
+        q.copy_(torch.randn(q.shape, generator=gen, device="cuda").to(q.dtype))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got_o, got_l = out.clone(), lse.clone()
+        ref_o, ref_l = tv.tree_verify_attn(q, d["k"], d["v"], d["parent"], d["prefix_len"],
+                                           maxl, num_splits=3)
+        torch.cuda.synchronize()
+        say("graph replay", rep, "max |diff|", float((got_o.float() - ref_o.float()).abs().max()))
+        assert torch.equal(got_o, ref_o) and torch.equal(got_l, ref_l), rep
