@@ -188,14 +188,15 @@ def test_node_count_sweep(N):
 
 # Small grids (at most one workgroup per compute unit) run the two-team build: every
 # four-wave shape -- one, two or three 16-node tiles per wave, with and without the shared
-# remainder tile -- over key ranges of 1 to 9 tiles, so a window is often half empty or
-# one team has no tile at all, with and without forced splits (several 32-key tiles per
+# remainder tile, and trees of one node and of exactly one full tile -- over key ranges of
+# 1 to 9 tiles, so a window is often half empty or one team has no tile at all, and one of
+# 32 tiles (eight windows), with and without forced splits (several 32-key tiles per
 # split, and splits of one chunk).
-@pytest.mark.parametrize("N", [10, 17, 32, 33, 48])
+@pytest.mark.parametrize("N", [1, 5, 10, 16, 17, 32, 33, 48])
 @pytest.mark.parametrize("splits", [0, 3])
-def test_two_team_shapes(N, splits):
-    paths, _ = random_trees(900 + N, 4, N, 8)
-    c = Case(f"teams_n{N}_s{splits}", [0, 20, 97, 240], trees=paths, seed=1500 + N)
+def test_team_shapes(N, splits):
+    paths, _ = random_trees(900 + N, 5, N, 8)
+    c = Case(f"teams_n{N}_s{splits}", [0, 20, 97, 240, 1000], trees=paths, seed=1500 + N)
     out, lse = c.run(num_splits=splits)
     c.check(out, lse)
 

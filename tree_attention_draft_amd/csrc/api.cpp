@@ -168,7 +168,7 @@ tv_status make_plan(const tv_attn_args* a, Plan* pl) {
     // are sized for one workgroup per compute unit instead: each workgroup pays a prologue
     // and a partial of R*(D+1)*4 bytes, which short chunks cannot hide (MI355X, L=2048,
     // B=8: 24.5 us at 4 splits against 25.7 at 6 and 25.9 at 8; paged L=32768, B=1, nine
-    // units a workgroup at two per unit: 59.4 us at 58 splits against 65.6 at 31).
+    // units a workgroup at two per unit: 59.4 us at 57 splits against 65.6 at 31).
     // Slots: two workgroups per compute unit, one for the eight-wave shapes (their register
     // use allows two waves per SIMD, i.e. eight waves per unit; B=16,
     // N=64, 64q/8kv: 152 us with one split against 183 us with the two that two slots

@@ -7,47 +7,52 @@
 // i.e. the softmax over the union of the chunks.  Requests with fewer splits than the grid
 // contribute only their own ceil((L + N) / chunk) partials; a request whose keys fit one
 // chunk was written directly by the attention kernel and is skipped here.
-// One thread per (request, kv head, packed row, 4 features).  The sum runs online over
-// groups of partials (16 while that many remain, then 4): all loads of a group are issued
-// before any of them is used (a thread walking many splits one at a time would wait a
-// memory round trip per split), and the running sum is moved to each group's max as it
-// goes.
+// Each output row (request, kv head, packed row) takes P * D/4 threads: thread (sub, q4)
+// owns 4 features and sums the partials of splits sub, sub + P, sub + 2P, ...; the P
+// subtotals then combine through LDS.  P grows with the grid's split count (about four
+// partials per thread), so a request split many ways is read by many threads at once
+// rather than by one thread per feature group walking every split.  Within a thread the
+// sum runs online over groups of partials (16 while that many remain, then 4): all loads
+// of a group are issued before any of them is used, and the running sum is moved to each
+// group's max as it goes.
 #include <type_traits>
 
 #include "kernels_common.h"
 
 namespace tv {
 
-template <typename T, int D>
+template <typename T, int D, int P>
 __global__ void __launch_bounds__(256) tv_merge_kernel(AttnParams p) {
   constexpr int Q4 = D / 4;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)p.B * p.Hkv * p.R * Q4;
-  if (gid >= total) return;
-  const int q4 = (int)(gid % Q4);
-  int64_t rest = gid / Q4;
-  const int row = (int)(rest % p.R);
-  rest /= p.R;
-  const int hkv = (int)(rest % p.Hkv);
-  const int b = (int)(rest / p.Hkv);
+  constexpr int RPW = 256 / (Q4 * P);  // rows per workgroup
+  static_assert(RPW >= 1 && RPW * Q4 * P == 256, "thread layout");
+  const int t = threadIdx.x;
+  const int q4 = t % Q4;
+  const int sub = (t / Q4) % P;
+  const int64_t gr = (int64_t)blockIdx.x * RPW + t / (Q4 * P);  // (request, kv head, row)
+  const int64_t rows = (int64_t)p.B * p.Hkv * p.R;
+  const int row = (int)(gr % p.R);
+  const int hkv = (int)((gr / p.R) % p.Hkv);
+  const int b = (int)min<int64_t>(gr / p.R / p.Hkv, p.B - 1);
   const int Ttot = clamped_prefix(p, b) + p.N;
-  const int ns = min(p.num_splits, (Ttot + p.chunk - 1) / p.chunk);
-  if (ns <= 1) return;  // one split: the attention kernel wrote the final output
+  // one split: the attention kernel wrote the final output (uniform over the row's threads)
+  const int ns = gr < rows ? min(p.num_splits, (Ttot + p.chunk - 1) / p.chunk) : 0;
 
   const int64_t base = ((int64_t)b * p.Hkv + hkv) * p.num_splits;
+  const int cnt = ns > 1 && ns > sub ? (ns - sub + P - 1) / P : 0;  // this thread's splits
   float mx = -INFINITY;  // max of the log-sum-exps seen so far
   float wsum = 0.f;      // sum of 2^(lse_s - mx) so far
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto group = [&](int s0, auto size_c) {
+  auto group = [&](int i0, auto size_c) {
     constexpr int G = decltype(size_c)::value;
     float ls[G];
     f32x4 v[G];
 #pragma unroll
     for (int u = 0; u < G; ++u) {
-      // past the last split: re-read the last partial (in bounds) and give it no weight
-      const int64_t prow = (base + min(s0 + u, ns - 1)) * p.R + row;
+      // past the thread's last split: re-read its last partial (in bounds), weight 0
+      const int64_t prow = (base + sub + (int64_t)P * min(i0 + u, cnt - 1)) * p.R + row;
       const float l = p.ws_lse[prow];
-      ls[u] = s0 + u < ns ? l : -INFINITY;
+      ls[u] = i0 + u < cnt ? l : -INFINITY;
       v[u] = *reinterpret_cast<const f32x4*>(p.ws_o + prow * D + 4 * q4);
     }
     float mg = mx;
@@ -66,9 +71,36 @@ __global__ void __launch_bounds__(256) tv_merge_kernel(AttnParams p) {
     }
     mx = mg;
   };
-  int s0 = 0;
-  for (; s0 + 16 <= ns; s0 += 16) group(s0, std::integral_constant<int, 16>{});
-  for (; s0 < ns; s0 += 4) group(s0, std::integral_constant<int, 4>{});
+  int i0 = 0;
+  for (; i0 + 16 <= cnt; i0 += 16) group(i0, std::integral_constant<int, 16>{});
+  for (; i0 < cnt; i0 += 4) group(i0, std::integral_constant<int, 4>{});
+
+  if constexpr (P > 1) {
+    // subtotals of the row's P thread groups, combined by sub = 0
+    __shared__ float sm[256], sw[256];
+    __shared__ f32x4 sa[256];
+    sm[t] = mx;
+    sw[t] = wsum;
+    sa[t] = acc;
+    __syncthreads();
+    if (sub != 0) return;
+    float M = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < P; ++u) M = fmaxf(M, sm[t + u * Q4]);
+    wsum = 0.f;
+    acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int u = 0; u < P; ++u) {
+        const float mu = sm[t + u * Q4];
+        const float sc = mu == -INFINITY ? 0.f : exp2f(mu - M);
+        wsum += sw[t + u * Q4] * sc;
+        acc += sa[t + u * Q4] * sc;
+      }
+    }
+    mx = M;
+  }
+  if (ns <= 1) return;
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   const int node = row / p.g, head = hkv * p.g + row % p.g;
   T* out = static_cast<T*>(p.out) + (int64_t)b * p.o_sb + (int64_t)node * p.o_sn +
@@ -87,18 +119,26 @@ __global__ void __launch_bounds__(256) tv_merge_kernel(AttnParams p) {
   }
 }
 
-hipError_t launch_merge(const AttnParams& p, int D, bool bf16, hipStream_t s) {
-  const int64_t total = (int64_t)p.B * p.Hkv * p.R * (D / 4);
-  const int threads = 256;
-  const unsigned blocks = (unsigned)((total + threads - 1) / threads);
-  if (bf16) {
-    if (D == 64) hipLaunchKernelGGL((tv_merge_kernel<uint16_t, 64>), dim3(blocks), dim3(threads), 0, s, p);
-    else hipLaunchKernelGGL((tv_merge_kernel<uint16_t, 128>), dim3(blocks), dim3(threads), 0, s, p);
-  } else {
-    if (D == 64) hipLaunchKernelGGL((tv_merge_kernel<float, 64>), dim3(blocks), dim3(threads), 0, s, p);
-    else hipLaunchKernelGGL((tv_merge_kernel<float, 128>), dim3(blocks), dim3(threads), 0, s, p);
+template <typename T, int D>
+static hipError_t launch_merge_p(const AttnParams& p, hipStream_t s) {
+  // thread groups per row: about four partials per thread, at most 8
+  int P = 1;
+  while (P < 8 && 8 * P <= p.num_splits) P *= 2;
+  const int64_t rows = (int64_t)p.B * p.Hkv * p.R;
+  const int64_t rpw = 256 / (D / 4 * P);
+  const unsigned blocks = (unsigned)((rows + rpw - 1) / rpw);
+  switch (P) {
+    case 1: hipLaunchKernelGGL((tv_merge_kernel<T, D, 1>), dim3(blocks), dim3(256), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((tv_merge_kernel<T, D, 2>), dim3(blocks), dim3(256), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((tv_merge_kernel<T, D, 4>), dim3(blocks), dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL((tv_merge_kernel<T, D, 8>), dim3(blocks), dim3(256), 0, s, p); break;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_merge(const AttnParams& p, int D, bool bf16, hipStream_t s) {
+  if (bf16) return D == 64 ? launch_merge_p<uint16_t, 64>(p, s) : launch_merge_p<uint16_t, 128>(p, s);
+  return D == 64 ? launch_merge_p<float, 64>(p, s) : launch_merge_p<float, 128>(p, s);
 }
 
 }  // namespace tv
