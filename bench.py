@@ -451,6 +451,7 @@ def main():
         ref = ometa.meta_from_parent(ref_parent[b], int(L[b]))
         assert dep_h[b].tolist() == ref["depth"] and pos_h[b].tolist() == ref["pos"], b
         assert [int(x) & (2 ** 64 - 1) for x in msk_h[b]] == ref["bitmask"], b
+    assert np.array_equal(h_depth, dep_h)  # host builder and the pass's export agree
     out_h = out.float().cpu().numpy()
     lse_h = lse.cpu().numpy()
     worst = 0.0
@@ -468,8 +469,8 @@ def main():
         torch.cuda.synchronize()
 
     alg_bytes = algorithmic_bytes(L, N, Hq, Hkv, D, 2, paged_page=page)
-    depths = [ometa.meta_from_parent(p, 0)["depth"] for p in ref_parent]
-    flops = algorithmic_flops(L, depths, Hq, D)
+    # node depths from the library's host builder (h_depth, checked above)
+    flops = algorithmic_flops(L, h_depth, Hq, D)
     achieved = alg_bytes / kern_avg_s / 1e9
     traffic = None
     if (args.workload == "b64_l4096_n33" and not args.batch and not args.rope_theta
