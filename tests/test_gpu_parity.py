@@ -247,10 +247,23 @@ def test_head_shapes_and_forced_paths(D, hq, hkv):
     assert np.abs(results["valu"] - results["mfma"]).max() <= 2e-2
 
 
-@pytest.mark.parametrize("splits", [1, 2, 7, 1000])
+# Requested split counts 1, 2, 7, 9, 20 and 1000 give grids of 1, 2, 7, 8, 16 and 64
+# splits over the longest request (64 chunks of 64 keys): the merge then spreads each
+# output's partials over 1, 2, 4 or 8 thread groups; the shorter requests have fewer
+# partials than the grid (and the 33-key one a single chunk, written directly).
+@pytest.mark.parametrize("splits", [1, 2, 7, 9, 20, 1000])
 def test_split_invariance(splits):
     paths, _ = random_trees(700, 3, 33, 8)
-    c = Case("splits", [1000, 999, 33], trees=paths, seed=1300)
+    c = Case("splits", [4000, 999, 33], trees=paths, seed=1300)
+    out, lse = c.run(num_splits=splits)
+    c.check(out, lse)
+
+
+@pytest.mark.parametrize("splits", [3, 1000])
+def test_split_invariance_d64(splits):
+    # D = 64: two output rows per merge workgroup at eight thread groups per output
+    paths, _ = random_trees(710, 3, 17, 8)
+    c = Case("splits_d64", [2500, 130, 700], trees=paths, Hq=16, Hkv=4, D=64, seed=1310)
     out, lse = c.run(num_splits=splits)
     c.check(out, lse)
 
