@@ -268,6 +268,32 @@ def test_split_invariance_d64(splits):
     c.check(out, lse)
 
 
+def test_prepared_call_matches_the_plain_call():
+    # arguments marshalled once, the call repeated with the same buffers: bit-identical to
+    # the plain call, also after the inputs change in place between calls
+    import torch
+    paths, _ = random_trees(720, 3, 33, 8)
+    c = Case("prepared", [900, 40, 3000], trees=paths, seed=1320)
+    d = c.device()
+    Lmax = int(c.L.max())
+    out = torch.empty_like(d["q"])
+    lse = torch.empty(d["q"].shape[:3], dtype=torch.float32, device="cuda")
+    call = tv.prepare_tree_verify_attn(d["q"], d["k"], d["v"], d["parent"], d["prefix_len"],
+                                       Lmax, out=out, lse=lse, num_splits=5)
+    for scale in (1.0, 0.5):
+        d["q"].mul_(scale)
+        want_o, want_l = tv.tree_verify_attn(d["q"], d["k"], d["v"], d["parent"],
+                                             d["prefix_len"], Lmax, num_splits=5)
+        got_o, got_l = call()
+        torch.cuda.synchronize()
+        assert got_o is out and got_l is lse
+        assert torch.equal(got_o, want_o) and torch.equal(got_l, want_l), scale
+    d["q"].mul_(2.0)  # back to the inputs the oracle reads (scaling by 0.5 and 2 is exact)
+    call()
+    torch.cuda.synchronize()
+    c.check(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64))
+
+
 def test_prefix_edges_in_one_batch():
     Ls = [0, 1, 63, 64, 65, 127, 128, 129, 5]
     paths, _ = random_trees(800, len(Ls), 33, 8)

@@ -434,6 +434,49 @@ def tree_verify_attn(q, k, v, parent, prefix_len, max_prefix_len, *, page_table=
     return out, lse
 
 
+class PreparedAttn:
+    """A ``tree_verify_attn`` call whose arguments are marshalled once: calling it only
+    enqueues the pass (the C call with the prepared struct), so a serving loop that reuses
+    the same buffers pays no per-call argument handling.  It keeps the tensors it was made
+    from alive; their contents may change between calls, their storage may not.  Calls on
+    one object share its output and workspace buffers: the caller orders them."""
+
+    def __init__(self, args, keep, stream):
+        self._a = args
+        self._keep = keep
+        self._stream = stream
+        self.out, self.lse = keep["out"], keep["lse"]
+
+    def __call__(self):
+        _check(lib().tree_verify_attn(ctypes.byref(self._a), self._stream))
+        return self.out, self.lse
+
+
+def prepare_tree_verify_attn(q, k, v, parent, prefix_len, max_prefix_len, *, out,
+                             lse=None, workspace=None, page_table=None, page_size=0,
+                             sm_scale=0.0, num_splits=0, path="auto", rope_theta=0.0,
+                             prefix_len_host=None, meta=None, stream=None):
+    """Marshal the arguments of ``tree_verify_attn`` once (same meaning) and return a
+    :class:`PreparedAttn` that launches the pass on ``stream`` (the current stream when
+    None) each time it is called.  ``out`` is required; the split workspace is taken from
+    ``workspace`` when it is large enough, else allocated here once."""
+    torch = _torch()
+    _require_cuda(q, k, v, prefix_len, page_table, out, lse, workspace)
+    a = make_args(q, k, v, parent, prefix_len, max_prefix_len, page_table=page_table,
+                  page_size=page_size, sm_scale=sm_scale, out=out, lse=lse,
+                  workspace=workspace, num_splits=num_splits, path=path,
+                  rope_theta=rope_theta, prefix_len_host=prefix_len_host, meta=meta)
+    need = int(lib().tree_verify_attn_workspace_size(ctypes.byref(a)))
+    if need > 0 and (workspace is None or a.workspace_bytes < need):
+        with _on(stream):
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = need
+    keep = dict(q=q, k=k, v=v, parent=parent, prefix_len=prefix_len, page_table=page_table,
+                out=out, lse=lse, workspace=workspace, meta=meta)
+    return PreparedAttn(a, keep, _stream(stream))
+
+
 STATIC_SCRATCH_BYTES = 64 * 1024 * 1024   # TV_STATIC_SCRATCH_BYTES
 
 
