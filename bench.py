@@ -415,20 +415,23 @@ def main():
     ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(total)]
     ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(total)]
     meta = (d_depth, d_mask, d_pos)
-    # The pass's arguments are marshalled once per (input copy, pinned slot), as a serving
-    # loop reusing its buffers would: a step then only enqueues the C call, and the events
-    # around it time the kernels rather than the binding's argument handling.
+    # The builder's and the pass's arguments are marshalled once per pinned slot (and input
+    # copy), as a serving loop reusing its buffers would: a step then runs the C builder and
+    # enqueues the C call, and the events around the latter time the kernels rather than
+    # the binding's argument handling.
     calls = [[tv.prepare_tree_verify_attn(qi, ki, vi, pin[s], prefix_dev, Lmax,
                                           page_table=pt_dev, page_size=page, out=out,
                                           lse=lse, workspace=ws, rope_theta=args.rope_theta,
                                           prefix_len_host=L, meta=meta)
               for s in range(2)] for qi, ki, vi in qkv]
 
+    builds = [tv.prepare_tree_meta_build_batch(packed, L, N, pin_np[s], h_depth, h_mask, h_pos)
+              for s in range(2)]
+
     def step(i):
         s = i % 2
         att_done[s].synchronize()         # the pass that last read this pinned slot is done
-        tv.tree_meta_build_batch(packed, L, N, parent=pin_np[s], depth=h_depth,
-                                 bitmask=h_mask, pos=h_pos)
+        builds[s]()                       # the host builder into this pinned slot
         ev_a[i].record()
         calls[i % n_copies][s]()
         ev_b[i].record()

@@ -145,3 +145,37 @@ def test_relabelled_duplicates_and_order_within_each_tree():
     L = rng.integers(0, 100, 6).astype(np.int32)
     got = tv.tree_meta_build_batch(PackedTrees(trees), L, 12)
     check_rows(trees, L, 12, got)
+
+
+def test_prepared_build_repeats_into_the_same_arrays():
+    # pointers resolved once; the prefix lengths and outputs keep their storage, and a
+    # second call after the lengths change in place rebuilds the position ids
+    rng = np.random.Generator(np.random.PCG64(73))
+    trees = [workloads.random_tree(rng, n, 8)[0] for n in (33, 5, 20)]
+    B, N = len(trees), 40
+    L = np.array([100, 0, 4096], np.int32)
+    out = {k: np.zeros((B, N), dt) for k, dt in (("parent", np.int32), ("depth", np.int32),
+                                                  ("bitmask", np.uint64), ("pos", np.int32))}
+    Lp = L.copy()   # the caller's int32 lengths are used in place, not copied
+    build = tv.prepare_tree_meta_build_batch(PackedTrees(trees), Lp, N, out["parent"],
+                                             out["depth"], out["bitmask"], out["pos"])
+    for shift in (0, 7):
+        Lp[:] = L + shift
+        build()
+        got = dict(out, num_nodes=build.num_nodes)
+        check_rows(trees, L + shift, N, got)
+
+
+def test_prepared_build_checks_its_outputs_and_reports_failures():
+    trees = [list(workloads.TEN_NODE_PATHS), [(0,), (1, 0)]]
+    good = np.zeros((2, 16), np.int32)
+    with pytest.raises(ValueError):
+        tv.prepare_tree_meta_build_batch(PackedTrees(trees), np.zeros(2, np.int32), 16,
+                                         good, good.copy(), np.zeros((2, 16), np.int64),
+                                         good.copy())
+    build = tv.prepare_tree_meta_build_batch(PackedTrees(trees), np.zeros(2, np.int32), 16,
+                                             good, good.copy(), np.zeros((2, 16), np.uint64),
+                                             good.copy())
+    with pytest.raises(TreeVerifyError) as e:
+        build()
+    assert e.value.name == "TV_ERR_MISSING_PARENT" and e.value.bad_tree == 1

@@ -249,6 +249,42 @@ def tree_meta_build_batch(packed, prefix_len, N, parent=None, depth=None, bitmas
             "num_nodes": nn}
 
 
+class PreparedBuild:
+    """A ``tree_meta_build_batch`` call with every pointer resolved once: calling it only
+    runs the C builder into the same output arrays (a serving loop's per-step metadata).
+    Keeps the packed trees, prefix lengths and outputs alive; their contents may change
+    between calls, their storage may not.  Prefix lengths given as a C-contiguous int32
+    array are read in place (otherwise from a copy made here)."""
+
+    def __init__(self, packed, prefix_len, N, parent, depth, bitmask, pos):
+        self._keep = (packed, np.ascontiguousarray(prefix_len, dtype=np.int32), parent,
+                      depth, bitmask, pos, np.empty(packed.B, np.int32))
+        pl, nn = self._keep[1], self._keep[6]
+        for a, dt in ((parent, np.int32), (depth, np.int32), (bitmask, np.uint64),
+                      (pos, np.int32)):
+            if a.dtype != dt or a.shape != (packed.B, N) or not a.flags.c_contiguous:
+                raise ValueError("outputs must be C-contiguous [B, N] int32/int32/uint64/int32")
+        self._bt, self._bp = ctypes.c_int32(-1), ctypes.c_int32(-1)
+        self._args = (packed.ranks.ctypes.data, packed.path_off.ctypes.data,
+                      packed.tree_off.ctypes.data, packed.B, pl.ctypes.data, int(N),
+                      parent.ctypes.data, depth.ctypes.data, bitmask.ctypes.data,
+                      pos.ctypes.data, nn.ctypes.data, ctypes.byref(self._bt),
+                      ctypes.byref(self._bp))
+        self.num_nodes = nn
+
+    def __call__(self):
+        st = lib().tree_meta_build_batch(*self._args)
+        if st != TV_OK:
+            raise TreeVerifyError(st, lib().tv_last_error().decode() +
+                                  f" (tree {self._bt.value})", self._bp.value, self._bt.value)
+
+
+def prepare_tree_meta_build_batch(packed, prefix_len, N, parent, depth, bitmask, pos):
+    """``tree_meta_build_batch`` into the given [B, N] host arrays (numpy, e.g. views of
+    pinned buffers), prepared once: returns a :class:`PreparedBuild`."""
+    return PreparedBuild(packed, prefix_len, N, parent, depth, bitmask, pos)
+
+
 # ------------------------------------------------------------------- device side -----
 def _torch():
     import torch
