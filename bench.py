@@ -407,10 +407,9 @@ def main():
     # pass reads them there in place (no copy, no second stream); the pass also writes the
     # expanded metadata (depth, bitmask, position ids) from its prologue.  A slot is
     # rewritten only after the pass that last read it has finished, so the builder of step
-    # k+1 overlaps the pass of step k.
-    att_done = [torch.cuda.Event() for _ in range(2)]
-    for e in att_done:
-        e.record()
+    # k+1 overlaps the pass of step k; the event that closes a pass's timing also marks its
+    # slot free (no third event on the stream between passes).
+    slot_done = [None, None]
     total = args.warmup + args.steps
     ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(total)]
     ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(total)]
@@ -430,12 +429,13 @@ def main():
 
     def step(i):
         s = i % 2
-        att_done[s].synchronize()         # the pass that last read this pinned slot is done
+        if slot_done[s] is not None:
+            slot_done[s].synchronize()    # the pass that last read this pinned slot is done
         builds[s]()                       # the host builder into this pinned slot
         ev_a[i].record()
         calls[i % n_copies][s]()
         ev_b[i].record()
-        att_done[s].record()
+        slot_done[s] = ev_b[i]
 
     print("[bench] warmup", file=sys.stderr, flush=True)
     for i in range(args.warmup):
