@@ -268,6 +268,16 @@ def test_split_invariance_d64(splits):
     c.check(out, lse)
 
 
+@pytest.mark.parametrize("splits", [12, 1000])
+def test_split_invariance_f32(splits):
+    # the vector path (fp32) with 2 and 8 merge thread groups per output (64-key chunks:
+    # 48 of them over the longest request)
+    c = Case("splits_f32", [3000, 64, 777], trees=TEN, Hq=4, Hkv=2, D=64, dtype="f32",
+             seed=1330)
+    out, lse = c.run(num_splits=splits)
+    c.check(out, lse)
+
+
 def test_prepared_call_matches_the_plain_call():
     # arguments marshalled once, the call repeated with the same buffers: bit-identical to
     # the plain call, also after the inputs change in place between calls
