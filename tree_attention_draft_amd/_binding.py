@@ -493,9 +493,10 @@ def prepare_tree_verify_attn(q, k, v, parent, prefix_len, max_prefix_len, *, out
                              sm_scale=0.0, num_splits=0, path="auto", rope_theta=0.0,
                              prefix_len_host=None, meta=None, stream=None):
     """Marshal the arguments of ``tree_verify_attn`` once (same meaning) and return a
-    :class:`PreparedAttn` that launches the pass on ``stream`` (the current stream when
-    None) each time it is called.  ``out`` is required; the split workspace is taken from
-    ``workspace`` when it is large enough, else allocated here once."""
+    :class:`PreparedAttn` that launches the pass on ``stream`` each time it is called
+    (when None, on the stream that is current now, at preparation, not at each call).
+    ``out`` is required; the split workspace is taken from ``workspace`` when it is large
+    enough, else allocated here once on that stream."""
     torch = _torch()
     _require_cuda(q, k, v, prefix_len, page_table, out, lse, workspace)
     a = make_args(q, k, v, parent, prefix_len, max_prefix_len, page_table=page_table,
