@@ -5,13 +5,16 @@
 // interviewers probe next"; "Tree Verification", "Accepting on a Tree").
 //
 // One 1024-thread workgroup per request walks its tree.  The distribution r a sibling is
-// judged against is never stored: after k applied rejections it is, per vocabulary entry,
-//   r_0 = p,  r_{j+1} = max(r_j / z_j - q, 0),
-// with z_j the total of r_j, so every test costs one pass over the node's p and q rows
-// (the total of the residual a rejection leaves is the next test's z) and the final draw
-// two.  All arithmetic is float64, every reduction in one fixed order per launch shape.
-// Each level divides by its total as one multiply-add with the total's reciprocal (one
-// division per level, not per entry), which differs from a division by at most an ulp,
+// judged against is never stored.  With r_0 = p and r_{j+1} = max(r_j / z_j - q, 0), z_j
+// the total of r_j, the residual after k applied rejections is, up to a positive scale,
+//   R_k = max(p - S_k q, 0),   S_k = Z_0 + ... + Z_{k-1},   Z_j the total of R_j
+// (R_{j+1} = max(R_j - Z_j q, 0) is z_0...z_j times r_{j+1}, and an entry once clipped to
+// zero stays there), and every use of r is scale-free: a child x is accepted when
+// u q(x) Z_k < R_k(x), and the final draw takes the first entry whose running sum of R_k
+// exceeds u Z_k.  So a test costs one pass over the node's p and q rows with one fma per
+// entry (the total of the residual a rejection leaves is the next test's Z) and the final
+// draw two.  All arithmetic is float64, every reduction in one fixed order per launch
+// shape; the closed form rounds differently from the iterated one only in the last bits,
 // the order of the differences the summation order already makes.
 #include <climits>
 
@@ -53,18 +56,14 @@ __device__ int block_extreme(int v, int* red) {
   return t;
 }
 
-// r_k at one vocabulary entry from its p and q values and the reciprocals of the k totals
-// applied so far.
-__device__ inline double residual_at(float pv, float qv, const double* inv, int levels) {
-  double r = static_cast<double>(pv);
-  const double qd = static_cast<double>(qv);
-  for (int j = 0; j < levels; ++j) r = fmax(fma(r, inv[j], -qd), 0.0);
-  return r;
+// R_k at one vocabulary entry from its p and q values and S_k (p itself before any
+// rejection has been applied).
+__device__ inline double residual_at(float pv, float qv, double S, int levels) {
+  const double pd = static_cast<double>(pv);
+  return levels == 0 ? pd : fmax(fma(-S, static_cast<double>(qv), pd), 0.0);
 }
 
-// Loads per thread issued together before any of them is used (the per-element arithmetic
-// holds a loop of runtime length, so the compiler would otherwise wait a memory round
-// trip per element).
+// Loads per thread issued together before any of them is used.
 constexpr int kBatch = 8;
 constexpr int kDraw = 8;  // consecutive entries per thread in the final draw's tiles
 
@@ -120,7 +119,6 @@ template <bool VEC>
 __global__ void __launch_bounds__(kWalkThreads) tv_stochastic_walk_kernel(SampleParams P) {
   __shared__ int32_t par[TV_MAX_NODES], tok[TV_MAX_NODES];
   __shared__ int32_t acc[TV_MAX_NODES], em[TV_MAX_NODES];
-  __shared__ double zs[TV_MAX_NODES];  // 1 / total of each applied rejection's r
   __shared__ double red[kWalkWaves];
   __shared__ int ired[kWalkWaves];
   __shared__ double scan[kWalkWaves];
@@ -143,6 +141,7 @@ __global__ void __launch_bounds__(kWalkThreads) tv_stochastic_walk_kernel(Sample
     const float* prow = P.p + (int64_t)b * P.p_sb + (int64_t)node * P.p_sn;
     const float* qrow = P.q + (int64_t)b * P.q_sb + (int64_t)node * P.q_sn;
     int levels = 0;
+    double S = 0.0;  // sum of the applied rejections' totals
     double z = block_sum(strided_sum<VEC, false>(prow, qrow, V,
                                             [](float pv, float) { return static_cast<double>(pv); }),
                          red);  // total of r_0 = p
@@ -151,25 +150,23 @@ __global__ void __launch_bounds__(kWalkThreads) tv_stochastic_walk_kernel(Sample
       if (par[c] != node) continue;
       const int x = tok[c];
       if (x < 0 || x >= V) continue;  // not a vocabulary entry: never accepted
-      const double rx = residual_at(prow[x], qrow[x], zs, levels);
+      const double rx = residual_at(prow[x], qrow[x], S, levels);
       if (u[c] * static_cast<double>(qrow[x]) * z < rx) {
         taken = c;
         break;
       }
       // rejected: the residual's total decides whether it replaces r
-      const double iz = 1.0 / z;
+      const double S1 = S + z;
       const double m = block_sum(
           strided_sum<VEC, true>(prow, qrow, V,
                             [&](float pv, float qv) {
-                              return fmax(fma(residual_at(pv, qv, zs, levels), iz,
-                                              -static_cast<double>(qv)),
+                              return fmax(fma(-S1, static_cast<double>(qv),
+                                              static_cast<double>(pv)),
                                           0.0);
                             }),
           red);
       if (m > 0.0) {
-        __syncthreads();  // every thread is done reading zs[0 .. levels)
-        if (tid == 0) zs[levels] = iz;
-        __syncthreads();
+        S = S1;
         ++levels;
         z = m;
       }
@@ -216,7 +213,7 @@ __global__ void __launch_bounds__(kWalkThreads) tv_stochastic_walk_kernel(Sample
       double own = 0.0;
 #pragma unroll
       for (int i = 0; i < kDraw; ++i) {
-        r[i] = v0 + i < V ? residual_at(pv[i], qv[i], zs, levels) : 0.0;
+        r[i] = v0 + i < V ? residual_at(pv[i], qv[i], S, levels) : 0.0;
         own += r[i];
         if (r[i] > 0.0) lastpos = v0 + i;
       }
