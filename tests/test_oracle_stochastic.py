@@ -203,3 +203,67 @@ def test_negative_control_siblings_against_raw_target(monkeypatch):
     T, Qm = markov_pair()
     counts = joint_of_three_tokens(np.random.default_rng(15), T, Qm, 30000)
     assert chi2_against_target(counts, T) > 4 * CHI2_26_999
+
+
+# ----------------------------------------------------- the residual in closed form -----
+def closed_form_residuals(p, q, k):
+    """max(p - S q, 0) after k rejections, S the sum of the earlier totals (unnormalised),
+    a rejection whose residual has no mass leaving everything unchanged."""
+    R, S = p.copy(), 0.0
+    out = [R]
+    for _ in range(k):
+        Z = R.sum()
+        nxt = np.maximum(p - (S + Z) * q, 0.0)
+        if nxt.sum() > 0:
+            S, R = S + Z, nxt
+        out.append(R)
+    return out
+
+
+def iterated_residuals(p, q, k):
+    r = p.copy()
+    out = [r]
+    for _ in range(k):
+        r = A._after_rejection(r, r.sum(), q)
+        out.append(r)
+    return out
+
+
+def residuals_agree(p, q, k):
+    for a, b in zip(iterated_residuals(p, q, k), closed_form_residuals(p, q, k)):
+        if not np.allclose(a / a.sum(), b / b.sum(), rtol=1e-12, atol=1e-15):
+            return False
+    return True
+
+
+def test_iterated_residual_equals_the_closed_form_up_to_scale():
+    # the normalised residual after k rejections is max(p - S_k q, 0) / its total, with S_k
+    # the running sum of the unnormalised totals: an identity independent of the
+    # oracle's iteration (the device walk evaluates this form)
+    rng = np.random.default_rng(16)
+    for trial in range(200):
+        V = int(rng.integers(2, 40))
+        p = rng.random(V) ** 3 * (0.5 + rng.random())   # unnormalised rows too
+        q = rng.random(V) ** 3
+        q /= q.sum()
+        if trial % 10 == 0:
+            # the no-mass corner a walk can reach: an unnormalised drafter row with excess
+            # mass everywhere (q = r / z exactly is not one: its children are always accepted)
+            q = 2.0 * p / p.sum()
+        assert residuals_agree(p, q, int(rng.integers(1, 12)))
+
+
+def test_negative_control_residual_without_normalising(monkeypatch):
+    # a residual that subtracts q from the unnormalised r breaks the identity
+    monkeypatch.setattr(A, "_after_rejection",
+                        lambda r, z, qn: np.maximum(r - qn, 0.0)
+                        if np.maximum(r - qn, 0.0).sum() > 0 else r)
+    rng = np.random.default_rng(17)
+    bad = 0
+    for _ in range(50):
+        V = int(rng.integers(4, 40))
+        p = rng.random(V) ** 3 * 3.0
+        q = rng.random(V) ** 3
+        q /= q.sum()
+        bad += not residuals_agree(p, q, 4)
+    assert bad > 25
