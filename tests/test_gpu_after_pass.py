@@ -201,3 +201,47 @@ def test_compaction_bit_exact(dtype, D, page_size):
         for b in range(B):
             T = int(L[b]) + N
             assert np.array_equal(kb[b, T:], k0[b, T:]) and np.array_equal(vb[b, T:], v0[b, T:])
+
+
+def test_prepared_calls_match_the_plain_calls():
+    # arguments marshalled once, calls repeated with the inputs changed in place: outputs
+    # equal to the plain calls' each time (greedy, stochastic, compaction)
+    import torch
+    B, N, V = 6, 17, 3001
+    parents = random_parents(880, B, N)
+    par = torch.tensor(np.array(parents, np.int32), device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(881)
+    logits = torch.randn((B, N, V), generator=g, device="cuda").to(torch.bfloat16)
+    tok = torch.randint(0, V, (B, N), generator=g, device="cuda", dtype=torch.int32)
+    greedy = tv.prepare_tree_accept_greedy(logits, tok, par)
+    p = torch.softmax(torch.randn((B, N, V), generator=g, device="cuda"), -1)
+    q = torch.softmax(torch.randn((B, N, V), generator=g, device="cuda"), -1)
+    u = torch.rand((B, N), generator=g, device="cuda", dtype=torch.float64)
+    stoch = tv.prepare_tree_accept_stochastic(p, q, tok, par, u)
+    for rep in range(2):
+        if rep:  # new inputs, same storage
+            logits.copy_(torch.randn((B, N, V), generator=g, device="cuda").to(torch.bfloat16))
+            p.copy_(torch.softmax(torch.randn((B, N, V), generator=g, device="cuda"), -1))
+            u.copy_(torch.rand((B, N), generator=g, device="cuda", dtype=torch.float64))
+        want = tv.tree_accept_greedy(logits, tok, par)
+        got = greedy()
+        want_s = tv.tree_accept_stochastic(p, q, tok, par, u)
+        got_s = stoch()
+        torch.cuda.synchronize()
+        for a, b in zip(got + got_s, want + want_s):
+            assert torch.equal(a, b), rep
+
+    # compaction: the same accepted lists applied to two copies of a cache
+    L, Hkv, D = 300, 4, 128
+    k = torch.randn((B, L + N, Hkv, D), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((B, L + N, Hkv, D), generator=g, device="cuda").to(torch.bfloat16)
+    k2, v2 = k.clone(), v.clone()
+    pl = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    _, acc, _, na = greedy.result
+    comp = tv.prepare_tree_kv_compact(k2, v2, pl, L, par, acc, na)
+    nl, st = tv.tree_kv_compact(k, v, pl, L, par, acc, na)
+    nl2, st2 = comp()
+    torch.cuda.synchronize()
+    assert torch.equal(nl, nl2) and torch.equal(st, st2)
+    assert torch.equal(k, k2) and torch.equal(v, v2)

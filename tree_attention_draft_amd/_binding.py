@@ -722,6 +722,74 @@ def tree_kv_compact(k, v, prefix_len, max_prefix_len, parent, accepted, num_acce
     return new_len, status
 
 
+class PreparedCall:
+    """An after-pass entry point whose arguments are marshalled once: calling it only makes
+    the C call (on the stream current at preparation, or the one given then) and returns
+    ``result``, the output tensors.  It keeps every tensor it was made from alive; their
+    contents may change between calls, their storage may not, and calls on one object
+    share its outputs and workspace: the caller orders them."""
+
+    def __init__(self, name, args, keep, stream, result):
+        self._name, self._a, self._keep, self._stream = name, args, keep, stream
+        self.result = result
+
+    def __call__(self):
+        _check(getattr(lib(), self._name)(ctypes.byref(self._a), self._stream))
+        return self.result
+
+
+def _outputs(dev, stream, shapes, given):
+    torch = _torch()
+    with _on(stream):
+        return tuple(torch.empty(sh, dtype=torch.int32, device=dev) if t is None else t
+                     for sh, t in zip(shapes, given))
+
+
+def prepare_tree_accept_greedy(logits, tokens, parent, target=None, accepted=None,
+                               emitted=None, num_accepted=None, workspace=None, stream=None):
+    """``tree_accept_greedy`` prepared once (same arguments); see :class:`PreparedCall`."""
+    _require_cuda(logits, tokens, parent, target, accepted, emitted, num_accepted, workspace)
+    B, N, _ = logits.shape
+    outs = _outputs(logits.device, stream, ((B, N), (B, N), (B, N), (B,)),
+                    (target, accepted, emitted, num_accepted))
+    a = make_accept_args(logits, tokens, parent, *outs)
+    need = int(lib().tree_accept_greedy_workspace_size(ctypes.byref(a)))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        with _on(stream):
+            workspace = _torch().empty(max(need, 16), dtype=_torch().uint8,
+                                       device=logits.device)
+    a.workspace = workspace.data_ptr()
+    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    return PreparedCall("tree_accept_greedy", a, (logits, tokens, parent, workspace),
+                        _stream(stream), outs)
+
+
+def prepare_tree_accept_stochastic(p, q, tokens, parent, uniform, accepted=None,
+                                   emitted=None, num_accepted=None, stream=None):
+    """``tree_accept_stochastic`` prepared once (same arguments); see :class:`PreparedCall`."""
+    _require_cuda(p, q, tokens, parent, uniform, accepted, emitted, num_accepted)
+    B, N, _ = p.shape
+    outs = _outputs(p.device, stream, ((B, N), (B, N), (B,)), (accepted, emitted, num_accepted))
+    a = make_sample_args(p, q, tokens, parent, uniform, *outs)
+    return PreparedCall("tree_accept_stochastic", a, (p, q, tokens, parent, uniform),
+                        _stream(stream), outs)
+
+
+def prepare_tree_kv_compact(k, v, prefix_len, max_prefix_len, parent, accepted, num_accepted,
+                            *, page_table=None, page_size=0, new_len=None, status=None,
+                            rope_theta=0.0, stream=None):
+    """``tree_kv_compact`` prepared once (same arguments); see :class:`PreparedCall`.  Each
+    call moves the rows the accepted lists name at that time, in place."""
+    _require_cuda(k, v, prefix_len, parent, accepted, num_accepted, page_table, new_len, status)
+    B = prefix_len.shape[0]
+    outs = _outputs(k.device, stream, ((B,), (B,)), (new_len, status))
+    a = make_compact_args(k, v, prefix_len, max_prefix_len, parent, accepted, num_accepted,
+                          page_table, page_size, *outs, rope_theta)
+    return PreparedCall("tree_kv_compact", a,
+                        (k, v, prefix_len, parent, accepted, num_accepted, page_table),
+                        _stream(stream), outs)
+
+
 # ------------------------------------------------------------------ budget policy ----
 def _probs(rank_prob):
     pr = np.ascontiguousarray(rank_prob, dtype=np.float64)
