@@ -10,6 +10,7 @@
 //                whose draft token equals it and continue there; stop when none does;
 //   compaction = K/V row L + a_j -> L + j for the accepted nodes a_0 = 0, a_1, ...
 #include "kernels_common.h"
+#include "mfma_common.h"
 
 namespace tv {
 
@@ -89,6 +90,22 @@ __global__ void __launch_bounds__(256) tv_argmax_kernel(const T* __restrict__ lo
   if (vec) {
     const int v0 = lo / E, v1 = hi / E;  // lo is a multiple of E
     const uint4* xv = reinterpret_cast<const uint4*>(x);
+    // A full slice is copied global -> LDS with non-temporal direct loads first (the logits
+    // are read once): each lane copies exactly the vectors it scans into the LDS slots it
+    // reads back, so its own wave's wait suffices and no barrier is needed.  The partial
+    // last slice is read from global memory directly.
+    constexpr int SV = kArgSlice / E;  // vectors of a full slice
+    static_assert(SV % (256 * kArgUnroll) == 0, "full slices split evenly over the loads");
+    __shared__ uint4 sbuf[SV];
+    const bool full = v1 - v0 == SV;  // uniform over the workgroup
+    if (full) {
+      const uint32_t sb = (uint32_t)(uintptr_t)(TV_LDS uint4*)sbuf;
+#pragma unroll
+      for (int u = 0; u < SV / 256; ++u)  // vector u*256 + tid into slot u*256 + tid
+        lds_load16(xv + v0 + u * 256 + tid, sb + (uint32_t)(u * 256 + (tid & ~63)) * 16u);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    auto vec_at = [&](int k) { return full ? sbuf[k - v0] : xv[k]; };
     float run = -INFINITY;
     int runk = -1;
     uint32_t mag = 0;  // bf16: two 16-bit lanes; f32: one 32-bit lane
@@ -96,7 +113,7 @@ __global__ void __launch_bounds__(256) tv_argmax_kernel(const T* __restrict__ lo
       uint4 w[kArgUnroll];
 #pragma unroll
       for (int u = 0; u < kArgUnroll; ++u)
-        if (k0 + 256 * u < v1) w[u] = xv[k0 + 256 * u];
+        if (k0 + 256 * u < v1) w[u] = vec_at(k0 + 256 * u);
 #pragma unroll
       for (int u = 0; u < kArgUnroll; ++u) {
         const int k = k0 + 256 * u;
@@ -123,7 +140,7 @@ __global__ void __launch_bounds__(256) tv_argmax_kernel(const T* __restrict__ lo
     const bool nan = BF ? ((mag & 0xffffu) > 0x7f80u || (mag >> 16) > 0x7f80u) : mag > 0x7f800000u;
     if (nan) {  // rare: the candidate is this thread's first NaN
       for (int k = v0 + tid; k < v1 && best.i == 0x7fffffff; k += 256) {
-        const uint4 wv = xv[k];
+        const uint4 wv = vec_at(k);
         const T* e = reinterpret_cast<const T*>(&wv);
         for (int t = 0; t < E; ++t) {
           const float f = static_cast<float>(e[t]);
@@ -134,7 +151,7 @@ __global__ void __launch_bounds__(256) tv_argmax_kernel(const T* __restrict__ lo
         }
       }
     } else if (runk >= 0) {  // the first element of the winning vector that equals its max
-      const uint4 wv = xv[runk];
+      const uint4 wv = vec_at(runk);
       const T* e = reinterpret_cast<const T*>(&wv);
       int t = E - 1;
 #pragma unroll
