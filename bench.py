@@ -127,6 +127,12 @@ class TimingEvents:
         assert self.hip.hipEventElapsedTime(self.ctypes.byref(ms), self.ev[i], self.ev[j]) == 0
         return ms.value
 
+    def close(self):
+        if self.hip is not None:
+            for e in self.ev:
+                self.hip.hipEventDestroy(e)
+            self.ev = []
+
 
 def blas_threads():
     try:
@@ -494,6 +500,7 @@ def main():
     t1 = time.perf_counter()
     elapsed = t1 - t0
     kern_ms = [ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(args.warmup, total)]
+    ev.close()
     kern_avg_s = float(np.mean(kern_ms)) / 1e3
 
     # metadata and a sampled parity check against the oracle (outside the timed region)

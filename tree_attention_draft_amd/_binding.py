@@ -479,12 +479,14 @@ class PreparedAttn:
 
     def __init__(self, args, keep, stream):
         self._a = args
+        self._ref = ctypes.byref(args)
+        self._fn = lib().tree_verify_attn
         self._keep = keep
         self._stream = stream
         self.out, self.lse = keep["out"], keep["lse"]
 
     def __call__(self):
-        _check(lib().tree_verify_attn(ctypes.byref(self._a), self._stream))
+        _check(self._fn(self._ref, self._stream))
         return self.out, self.lse
 
 
@@ -730,11 +732,12 @@ class PreparedCall:
     share its outputs and workspace: the caller orders them."""
 
     def __init__(self, name, args, keep, stream, result):
-        self._name, self._a, self._keep, self._stream = name, args, keep, stream
+        self._fn, self._a, self._keep, self._stream = getattr(lib(), name), args, keep, stream
+        self._ref = ctypes.byref(args)
         self.result = result
 
     def __call__(self):
-        _check(getattr(lib(), self._name)(ctypes.byref(self._a), self._stream))
+        _check(self._fn(self._ref, self._stream))
         return self.result
 
 
