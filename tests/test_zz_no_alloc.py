@@ -44,13 +44,18 @@ def reference_call(c, **kw):
     return out, lse
 
 
-@pytest.mark.parametrize("kind", ["mfma", "valu_f32"])
+@pytest.mark.parametrize("kind", ["mfma", "mfma_many_splits", "valu_f32"])
 def test_static_entry_point_two_calls(kind):
     if kind == "mfma":
         big = Case("static_big", [3000, 1500, 64, 2500, 777], trees=trees(7701, 5, 33, 8),
                    seed=7702)
         small = Case("static_small", [900, 40], trees=trees(7703, 2, 17, 6), seed=7704)
         kw_big, kw_small = dict(num_splits=6), dict(num_splits=3)
+    elif kind == "mfma_many_splits":
+        # 40 and 12 splits: the merge spreads each output over 8, then 2, thread groups
+        big = Case("static_many", [3000, 2500], trees=trees(7711, 2, 33, 8), seed=7712)
+        small = Case("static_many_small", [900, 40], trees=trees(7713, 2, 17, 6), seed=7714)
+        kw_big, kw_small = dict(num_splits=40), dict(num_splits=12)
     else:
         big = Case("static_big_f32", [700, 333, 1200], trees=trees(7705, 3, 20, 6), Hq=8,
                    Hkv=2, dtype="f32", seed=7706)
