@@ -14,6 +14,11 @@ per step.  Inputs are seeded synthetic Gaussians and sit in HBM before timing st
 working set exceeds the 256 MB last-level cache, so no flush is needed between steps.
 
 Prints ONE JSON line.  ``value`` = verified tree nodes per second over the timed steps.
+After them a longer run of the same steps (``--steady-warmup`` untimed, ``--steady-steps``
+timed) is reported under ``steady_state``: the board's power management slows the shader
+clock for the first ~250 launches after an idle period, so a short run from idle and a
+serving loop that runs continuously see different rates.  That leg's final output must
+equal the timed steps' output bit for bit.
 """
 import argparse
 import hashlib
@@ -378,6 +383,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steady-warmup", type=int, default=400,
+                    help="untimed steps before the steady-state leg")
+    ap.add_argument("--steady-steps", type=int, default=1000,
+                    help="timed steps of the steady-state leg (0: skip it)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -463,7 +472,8 @@ def main():
     # slot free (no third event on the stream between passes).
     slot_done = [None, None]
     total = args.warmup + args.steps
-    ev = TimingEvents(2 * total)  # launch i between events 2i and 2i+1
+    n_steady = args.steady_warmup + args.steady_steps if args.steady_steps > 0 else 0
+    ev = TimingEvents(2 * (total + n_steady))  # launch i between events 2i and 2i+1
     meta = (d_depth, d_mask, d_pos)
     # The builder's and the pass's arguments are marshalled once per pinned slot (and input
     # copy), as a serving loop reusing its buffers would: a step then runs the C builder and
@@ -500,8 +510,34 @@ def main():
     t1 = time.perf_counter()
     elapsed = t1 - t0
     kern_ms = [ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(args.warmup, total)]
-    ev.close()
     kern_avg_s = float(np.mean(kern_ms)) / 1e3
+
+    steady = None
+    if n_steady:
+        # the same steps continued, past the clock transient that follows an idle GPU
+        out_t, lse_t = out.clone(), lse.clone()
+        print("[bench] steady-state leg", file=sys.stderr, flush=True)
+        for i in range(total, total + args.steady_warmup):
+            step(i)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for i in range(total + args.steady_warmup, total + n_steady):
+            step(i)
+        torch.cuda.synchronize()
+        t3 = time.perf_counter()
+        st_ms = [ev.elapsed_ms(2 * i, 2 * i + 1)
+                 for i in range(total + args.steady_warmup, total + n_steady)]
+        st_avg_s = float(np.mean(st_ms)) / 1e3
+        same = bool(torch.equal(out, out_t) and torch.equal(lse, lse_t))
+        del out_t, lse_t
+        steady = {"warmup": args.steady_warmup, "steps": args.steady_steps,
+                  "value": B * N * args.steady_steps / (t3 - t2),
+                  "ms_per_step": (t3 - t2) / args.steady_steps * 1e3,
+                  "kernel_avg_us": st_avg_s * 1e6,
+                  "kernel_p10_p50_p90_us": [float(np.percentile(st_ms, x)) * 1e3
+                                            for x in (10, 50, 90)],
+                  "output_identical": same}
+    ev.close()
 
     # metadata and a sampled parity check against the oracle (outside the timed region)
     ref_parent = [ometa.build_from_paths(t, 0)["parent"] for t in trees]
@@ -519,7 +555,7 @@ def main():
     for b in sample:
         o, l = oracle_request(host, b, ref_parent[b], L[b], N, page, args.rope_theta)
         worst = max(worst, float(np.abs(out_h[b] - o).max()), float(np.abs(lse_h[b] - l).max()))
-    parity_ok = worst <= 2e-2
+    parity_ok = worst <= 2e-2 and (steady is None or steady["output_identical"])
 
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -578,6 +614,11 @@ def main():
         "parity": {"requests": sample, "max_abs_err": worst, "tol": 2e-2, "ok": parity_ok},
         "cpu_baseline": None,
     }
+    if steady is not None:
+        st_gbs = alg_bytes / (steady["kernel_avg_us"] * 1e-6) / 1e9
+        steady.update({"achieved": st_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": st_gbs / HBM_PEAK_GBS})
+        result["steady_state"] = steady
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(host, ref_parent, L, N, args.cpu_seconds, page,
