@@ -616,8 +616,10 @@ def main():
     }
     if steady is not None:
         st_gbs = alg_bytes / (steady["kernel_avg_us"] * 1e-6) / 1e9
+        st_tflops = flops / (steady["kernel_avg_us"] * 1e-6) / 1e12
         steady.update({"achieved": st_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                       "frac": st_gbs / HBM_PEAK_GBS})
+                       "frac": st_gbs / HBM_PEAK_GBS, "mfma_tflops": st_tflops,
+                       "mfma_frac": st_tflops / MFMA_BF16_PEAK_TFLOPS})
         result["steady_state"] = steady
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
