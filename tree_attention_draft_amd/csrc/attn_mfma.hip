@@ -292,8 +292,7 @@ template <class C, int KT, int NST, int WIN>
 __device__ inline void rope_tree_keys(char* smem, int it, int ntiles, int kbeg, int kend,
                                       int L, const uint64_t* mask_s, const double* inv_freq,
                                       int tid, int nthreads) {
-  constexpr int H = C::CH * 4;  // D / 2 pairs per row
-  constexpr int D = 2 * H;
+  constexpr int H = C::CH * 4;  // pairs per row: half the row's features
   const int t_lo = max(L, kbeg + it * KT);
   const int t_hi = min(kend, kbeg + min(it + WIN, ntiles) * KT);
 #pragma unroll 1
