@@ -35,7 +35,8 @@ METRIC = "tree-verify attn: verified nodes/s + HBM GB/s % peak at B=64,L=4k,N=33
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 COUNTERS = os.path.join(ROOT, "profiles", "tv_attn_mfma_b64_l4096_n33.counters.json")
-KERNEL_SOURCES = ["attn_mfma.hip", "mfma_common.h", "kernels_common.h", "tv_internal.h"]
+KERNEL_SOURCES = ["attn_mfma.h", "attn_mfma.hip", "mfma_common.h", "kernels_common.h",
+                  "tv_internal.h"]
 
 
 def kernel_source_hash():

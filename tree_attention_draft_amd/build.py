@@ -18,7 +18,7 @@ OUT = os.path.join(PKG, "libtreeverify.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.cpp", "tree_meta.cpp", "meta_device.hip", "attn_valu.hip", "attn_mfma.hip",
-           "merge.hip", "accept.hip", "sample.hip", "budget.cpp",
+           "attn_mfma_paged.hip", "merge.hip", "accept.hip", "sample.hip", "budget.cpp",
            "static_scratch.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

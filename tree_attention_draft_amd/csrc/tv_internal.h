@@ -126,6 +126,7 @@ hipError_t launch_compact(const CompactParams& p, hipStream_t s);
 hipError_t launch_stochastic_walk(const SampleParams& p, hipStream_t s);
 
 hipError_t launch_attn_mfma(const AttnParams& p, int D, MfmaShape shape, hipStream_t s);
+hipError_t launch_attn_mfma_paged(const AttnParams& p, int D, MfmaShape shape, hipStream_t s);
 hipError_t launch_attn_valu(const AttnParams& p, int D, bool bf16, hipStream_t s);
 hipError_t launch_merge(const AttnParams& p, int D, bool bf16, hipStream_t s);
 hipError_t launch_meta_from_parent(const int32_t* parent, int32_t parent_sb, int32_t B,
