@@ -12,9 +12,9 @@
 // subtotals then combine through LDS.  P grows with the grid's split count (about four
 // partials per thread), so a request split many ways is read by many threads at once
 // rather than by one thread per feature group walking every split.  Within a thread the
-// sum runs online over groups of partials (16 while that many remain, then 4): all loads
-// of a group are issued before any of them is used, and the running sum is moved to each
-// group's max as it goes.
+// sum runs online over groups of partials (16 while that many remain, then one group of
+// 16, 8 or 4 for the rest): all loads of a group are issued before any of them is used,
+// and the running sum is moved to each group's max as it goes.
 #include <type_traits>
 
 #include "kernels_common.h"
@@ -73,7 +73,14 @@ __global__ void __launch_bounds__(256) tv_merge_kernel(AttnParams p) {
   };
   int i0 = 0;
   for (; i0 + 16 <= cnt; i0 += 16) group(i0, std::integral_constant<int, 16>{});
-  for (; i0 < cnt; i0 += 4) group(i0, std::integral_constant<int, 4>{});
+  // the rest in one group sized to it (its surplus slots re-read the last partial)
+  const int rest = cnt - i0;
+  if (rest > 8)
+    group(i0, std::integral_constant<int, 16>{});
+  else if (rest > 4)
+    group(i0, std::integral_constant<int, 8>{});
+  else if (rest > 0)
+    group(i0, std::integral_constant<int, 4>{});
 
   if constexpr (P > 1) {
     // subtotals of the row's P thread groups, combined by sub = 0
