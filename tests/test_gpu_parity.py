@@ -567,6 +567,32 @@ def test_paged_page_sizes(page_size, D):
         c.check(out, lse)
 
 
+@pytest.mark.parametrize("splits", [4, 8])
+def test_paged_equals_contiguous_bit_for_bit(splits):
+    # The paged and contiguous instantiations differ only in how a tile's rows are
+    # addressed, so the same keys in either layout give the same bits (same split plan:
+    # every split fits the page-table slice).  Eight splits make 320 workgroups, more than
+    # one per compute unit, so the paged tiles take the vector-address form; four make 160,
+    # which run two teams per workgroup and the scalar form.
+    import torch
+    paths, _ = random_trees(2400, 5, 33, 8)
+    c = Case("paged_vs_contig", [1500, 33, 4000, 700, 2222], trees=paths, seed=2401,
+             page_size=16, page_seed=3401)
+    d = c.device()
+    out_p, lse_p = c.run(num_splits=splits)
+    table = d["page_table"].long()
+    B, pages = table.shape
+    k_c = d["k"][table].reshape(B, pages * 16, c.Hkv, c.D).contiguous()
+    v_c = d["v"][table].reshape(B, pages * 16, c.Hkv, c.D).contiguous()
+    say(c.name, "contiguous copy", {"num_splits": splits})
+    out_c, lse_c = tv.tree_verify_attn(d["q"], k_c, v_c, d["parent"], d["prefix_len"],
+                                       max_prefix_len=int(c.L.max()), num_splits=splits)
+    torch.cuda.synchronize()
+    assert np.array_equal(out_p, out_c.float().cpu().numpy().astype(np.float64))
+    assert np.array_equal(lse_p, lse_c.cpu().numpy().astype(np.float64))
+    c.check(out_p, lse_p)
+
+
 def test_paged_small_full_with_splits():
     spec = workloads.WORKLOADS["long_paged_n33"]
     trees, _ = workloads.trees_for(spec, batch=4)
