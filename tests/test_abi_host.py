@@ -289,13 +289,12 @@ def test_split_plan_from_host_lengths():
     R, D, Hkv = 33 * 4, 128, 8
     # without the lengths the plan sees 64 requests of 8192 keys: they fill the slots
     assert L.tree_verify_attn_workspace_size(ctypes.byref(ragged_args(ragged, False))) == 0
-    # with them it sizes chunks to two thirds of the average work (44 of 66 key tiles per
-    # workgroup slot) and splits the long requests in up to three
+    # with them it sizes chunks to the average work per workgroup slot (74 key tiles) and
+    # splits the long requests in two
     work = sum((int(x) + 33 + 63) // 64 for x in ragged) * Hkv
-    avg = -(-work // 512)
-    chunk = (2 * avg + 2) // 3
+    chunk = -(-work // 512)
     S = -(-129 // chunk)
-    assert S == 3
+    assert chunk == 74 and S == 2
     got = L.tree_verify_attn_workspace_size(ctypes.byref(ragged_args(ragged, True)))
     assert got == 64 * Hkv * S * R * (D + 1) * 4
     # equal lengths: the hint changes nothing

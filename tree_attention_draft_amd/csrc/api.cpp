@@ -160,10 +160,11 @@ tv_status make_plan(const tv_attn_args* a, Plan* pl) {
   } else {
     // chunks of the batch's average work per workgroup slot (two per compute unit): a
     // batch of equal requests that fills the slots keeps one split, smaller ones split
-    // until they fill them.  A ragged batch (lengths known from the host copy) takes
-    // chunks of two thirds of that average, so that its long requests spread over several
-    // workgroups taken first (on MI355X, B=64, L ~ U[512, 8192]: 264 us against 281 us
-    // with one split and 323 us with chunks of the average)
+    // until they fill them.  A ragged batch (lengths known from the host copy) is cut the
+    // same way, its pieces then taken longest first (on MI355X, L ~ U[512, 8192], back to
+    // back: B=64 246.9 us against 255.2 us with chunks of two thirds of the average, B=32
+    // 132.3 against 139.2 us; after an idle GPU, where the clock is cut, 315.5 against
+    // 317.2 us)
     // When that leaves a workgroup under 8 chunk units of 64 keys (small batches), chunks
     // are sized for one workgroup per compute unit instead: each workgroup pays a prologue
     // and a partial of R*(D+1)*4 bytes, which short chunks cannot hide (MI355X, L=2048,
@@ -177,7 +178,7 @@ tv_status make_plan(const tv_attn_args* a, Plan* pl) {
     const int64_t per_cu = pl->mfma && pl->shape.nw >= 8 ? 1 : 2;
     int64_t avg = (pair_tiles + per_cu * cus - 1) / (per_cu * cus);
     if (avg < 8) avg = (pair_tiles + cus - 1) / cus;
-    const int64_t chunk_tiles = std::max<int64_t>(1, ragged ? (2 * avg + 2) / 3 : avg);
+    const int64_t chunk_tiles = std::max<int64_t>(1, avg);
     S = (tiles + chunk_tiles - 1) / chunk_tiles;
   }
   S = std::max<int64_t>(S, 1);
