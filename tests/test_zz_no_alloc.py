@@ -44,7 +44,7 @@ def reference_call(c, **kw):
     return out, lse
 
 
-@pytest.mark.parametrize("kind", ["mfma", "mfma_many_splits", "valu_f32"])
+@pytest.mark.parametrize("kind", ["mfma", "mfma_many_splits", "mfma_paged", "valu_f32"])
 def test_static_entry_point_two_calls(kind):
     if kind == "mfma":
         big = Case("static_big", [3000, 1500, 64, 2500, 777], trees=trees(7701, 5, 33, 8),
@@ -56,6 +56,16 @@ def test_static_entry_point_two_calls(kind):
         big = Case("static_many", [3000, 2500], trees=trees(7711, 2, 33, 8), seed=7712)
         small = Case("static_many_small", [900, 40], trees=trees(7713, 2, 17, 6), seed=7714)
         kw_big, kw_small = dict(num_splits=40), dict(num_splits=12)
+    elif kind == "mfma_paged":
+        # paged KV (pages of 16): eight splits of five requests run one team per workgroup
+        # and the vector page addresses, three splits of two requests two teams and the
+        # scalar ones
+        big = Case("static_paged", [3000, 1500, 64, 2500, 777], trees=trees(7715, 5, 33, 8),
+                   seed=7716, page_size=16, page_seed=7717)
+        small = Case("static_paged_small", [900, 40], trees=trees(7718, 2, 33, 8), seed=7719,
+                     page_size=16, page_seed=7720)
+        kw_big = dict(num_splits=8, page_table=big.device()["page_table"], page_size=16)
+        kw_small = dict(num_splits=3, page_table=small.device()["page_table"], page_size=16)
     else:
         big = Case("static_big_f32", [700, 333, 1200], trees=trees(7705, 3, 20, 6), Hq=8,
                    Hkv=2, dtype="f32", seed=7706)
