@@ -441,6 +441,28 @@ __global__ void __launch_bounds__(NW * 64 * TEAMS, TEAMS == 1 ? 2 : 1)
   const char* vg = static_cast<const char*>(p.v);
   const uint32_t sbase = (uint32_t)(uintptr_t)(TV_LDS char*)smem;
 
+  // Two-team shapes (grids of at most one workgroup per compute unit) over contiguous KV:
+  // this team's full tiles of the first window go out before the prologue's own loads, so
+  // that their latency overlaps the query loads and the ancestor walk; the prologue's final
+  // wait drains them with its own loads.  The ring is idle until the key loop (fused RoPE
+  // uses it as scratch, so it keeps the order below).  Larger grids keep that order too:
+  // there every workgroup's early tiles only queue behind the others' (1-3% slower).
+  constexpr bool EARLY = TEAMS == 2 && !ROPE && !PG;
+  if constexpr (EARLY) {
+    if (!p.paged && (int64_t)(KT - 1) * p.kv_st * 2 + 2 * D <= INT32_MAX) {
+      const LoadPlan<C, NW> lpe(p, w, lane);
+      RowMap rme;
+      rme.pt = pt_s;
+      rme.pbase = 0;
+      rme.head_off = (int64_t)b * p.kv_sb + (int64_t)hkv * p.kv_sh;
+#pragma unroll
+      for (int s = 0; s < 2 * TEAMS; ++s)  // window 0: two tiles per team
+        if (s / 2 == team && s < ntiles && kbeg + (s + 1) * KT <= kend)
+          issue_tile<C, NW, KT, false>(p, rme, lpe, kg, vg, sbase + s * C::STAGEB, kbeg + s * KT,
+                                       kend, true, false, w, lane);
+    }
+  }
+
   // ---- prologue: every compiler-visible global load (Q, parent array, page-table slice)
   // happens here and is drained by one explicit wait before the asm-issued ring starts;
   // otherwise the compiler would guard later uses of these registers with vmcnt(0) and
@@ -561,9 +583,11 @@ __global__ void __launch_bounds__(NW * 64 * TEAMS, TEAMS == 1 ? 2 : 1)
   constexpr bool VA = PG && TEAMS == 1 && !(ROPE && TN >= 3);
   const bool fast = !PG && !p.paged && off32;
   const bool pfast = p.paged && off32 && p.page_shift >= 0 && p.page_size % C::RPI == 0;
+  static_assert(!EARLY || WIN == 2, "the early issue assumes two-tile windows");
 #pragma unroll
   for (int s = 0; s < NST; ++s)
-    if (s < ntiles && (s / WIN) % TEAMS == team)
+    if (s < ntiles && (s / WIN) % TEAMS == team &&
+        !(EARLY && fast && s < SW && kbeg + (s + 1) * KT <= kend))  // not issued early
       issue_tile<C, NW, KT, VA>(p, rm, lp, kg, vg, sbase + s * C::STAGEB, kbeg + s * KT, kend,
                                 fast, pfast, w, lane);
 
